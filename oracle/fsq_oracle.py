@@ -1,0 +1,231 @@
+"""Plain, slow fp64 CPU oracle for Transformer-FSQ latent decode.
+
+TEST INFRASTRUCTURE ONLY. Only the test-suite, the smoke check and the CPU
+baseline leg of the bench may import this module. The product path (the HIP
+library and its binding) never calls it and shares no code with it.
+
+What it computes, and where the pages define it (page titles as cited):
+  * "Transformer-FSQ: Discrete Latents for Extreme KV-Cache Compression"
+    (picx.dev summary), Theoretical Basis, Eq. 2 (the FSQ bound and round) and
+    Eq. 3 (the implicit product grid); Architecture, Eq. 4 (z = Q_FSQ(E x)) and
+    Eq. 5 (k = W_k z, v = W_v z, here without key norm and RoPE);
+    Key Design Innovation, Eq. 6 (values decoded once after pooling codes);
+    Byte Budgeting (c_full = 2 n_kv d_h sizeof(fp16)).
+  * Slides "Transformer-FSQ" (slides.en.tex), frame "A wide product code uses
+    four bits per coordinate": h = 7.5075, delta = 0.5 for L = 16, and the cache
+    size ceil(G b / 8) bytes per token per layer; frame "Attention pools codes
+    before decoding values" (Eq. 5-6 again).
+  * Query absorption q~_h = W_k,g(h)^T q_h is not on the pages; it is exact for
+    the linear key map W_k z used here and is pinned against materialised K/V.
+
+Readings of points the pages leave open:
+  * level values are the integers round(u~) in {-8..7}; code = level + 8;
+  * rounding is to nearest with ties to even (numpy.rint);
+  * byte j of a token holds code[2j] in its low nibble and code[2j+1] in its
+    high nibble; for odd G the last high nibble is zero;
+  * attention scale 1/sqrt(d_h); q head h reads kv head h // (n_q // n_kv);
+  * W_kv rows are [W_k; W_v], each kv-head-major with d_h rows per head;
+  * a sequence of length 0 produces a zero output.
+
+Every computation is fp64 on the exact values of the bf16 inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# L = 16 levels per coordinate -> 4 bits; constants printed on the slides,
+# frame "A wide product code uses four bits per coordinate" (footnote).
+LEVELS = 16
+BITS = 4
+H_BOUND = 7.5075
+DELTA = 0.5
+CODE_OFFSET = LEVELS // 2     # code = level + 8
+
+
+# ----------------------------------------------------------------- Eq. 2 / 3
+def fsq_bound(u, h: float = H_BOUND, delta: float = DELTA) -> np.ndarray:
+    """Bounded coordinate of Eq. 2: u~ = h * tanh(u + atanh(delta / h)) - delta."""
+    u = np.asarray(u, dtype=np.float64)
+    return h * np.tanh(u + math.atanh(delta / h)) - delta
+
+
+def fsq_levels(u) -> np.ndarray:
+    """Forward value of Eq. 2: the rounded bounded coordinate round(u~).
+
+    The straight-through term sg(round(u~) - u~) only changes gradients; in the
+    forward pass u^ equals round(u~) exactly. Result is an int64 level in -8..7."""
+    lv = np.rint(fsq_bound(u))
+    if lv.size and (lv.min() < -CODE_OFFSET or lv.max() > CODE_OFFSET - 1):
+        raise AssertionError("FSQ level outside -8..7")
+    return lv.astype(np.int64)
+
+
+def fsq_codes(u) -> np.ndarray:
+    """Code of each coordinate: level + 8, a value in 0..15 (uint8)."""
+    return (fsq_levels(u) + CODE_OFFSET).astype(np.uint8)
+
+
+def encode(x, E) -> np.ndarray:
+    """Eq. 4: z_t = Q_FSQ(E x_t) for every row x_t of x.
+
+    x [N, C] and E [G, C] as float64 (the exact bf16 values). Returns codes
+    [N, G] uint8. The projection is the fp64 matrix product u = x E^T."""
+    x = np.asarray(x, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    u = x @ E.T
+    return fsq_codes(u)
+
+
+def projection(x, E) -> np.ndarray:
+    """u = x E^T in fp64 (the argument of the quantiser in Eq. 4)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(E, dtype=np.float64).T
+
+
+# --------------------------------------------------------------- bytes, packing
+def bytes_per_token(G: int, bits: int = BITS) -> int:
+    """Cache size per token per layer, ceil(G * b / 8) bytes (slides, frame
+    "A wide product code uses four bits per coordinate")."""
+    return -(-(G * bits) // 8)
+
+
+def full_cache_bytes(n_kv: int, d_h: int, elem_bytes: int = 2) -> int:
+    """Uncompressed K/V bytes per token per layer, 2 * n_kv * d_h * sizeof(fp16)
+    (picx.dev summary, Byte Budgeting)."""
+    return 2 * n_kv * d_h * elem_bytes
+
+
+def pack_codes(codes) -> np.ndarray:
+    """[N, G] codes in 0..15 -> [N, ceil(G/2)] bytes; byte j = c[2j] | c[2j+1] << 4."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, G = codes.shape
+    if codes.size and codes.max() > 15:
+        raise AssertionError("code outside 0..15")
+    P = bytes_per_token(G)
+    padded = np.zeros((N, 2 * P), dtype=np.uint8)
+    padded[:, :G] = codes
+    out = np.zeros((N, P), dtype=np.uint8)
+    for j in range(P):
+        out[:, j] = padded[:, 2 * j] | (padded[:, 2 * j + 1] << 4)
+    return out
+
+
+def unpack_codes(packed, G: int) -> np.ndarray:
+    """Inverse of pack_codes: [N, ceil(G/2)] bytes -> [N, G] codes."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, P = packed.shape
+    if P != bytes_per_token(G):
+        raise ValueError("packed width does not match G")
+    out = np.zeros((N, 2 * P), dtype=np.uint8)
+    for j in range(P):
+        out[:, 2 * j] = packed[:, j] & 0x0F
+        out[:, 2 * j + 1] = packed[:, j] >> 4
+    return out[:, :G]
+
+
+def levels_of_codes(codes) -> np.ndarray:
+    """Latent values z = code - 8 as float64 (the grid points of Eq. 3)."""
+    return np.asarray(codes, dtype=np.float64) - CODE_OFFSET
+
+
+# ------------------------------------------------------- latent-space decode
+def _kv_head(h: int, n_q: int, n_kv: int) -> int:
+    return h // (n_q // n_kv)
+
+
+def decoder_blocks(W_kv, g: int, n_kv: int, d_h: int):
+    """W_k,g and W_v,g: the d_h rows of kv head g in the key and value halves
+    of W_kv = [W_k; W_v] (picx.dev summary, Eq. 8 row order)."""
+    W_kv = np.asarray(W_kv, dtype=np.float64)
+    Wk = W_kv[g * d_h:(g + 1) * d_h, :]
+    Wv = W_kv[n_kv * d_h + g * d_h:n_kv * d_h + (g + 1) * d_h, :]
+    return Wk, Wv
+
+
+def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
+    """One decode step of latent-space attention.
+
+    q [B, n_q, d_h], packed [B, cap, ceil(G/2)] bytes, W_kv [2 n_kv d_h, G],
+    seq_lens [B]. For each sequence b and query head h (kv head g):
+      q~ = W_k,g^T q                 (absorbed query; exact for k = W_k z)
+      s_t = q~ . z_t / sqrt(d_h)     for t < seq_lens[b]
+      p = softmax(s)
+      zbar = sum_t p_t z_t           (pool codes, Eq. 6)
+      out = W_v,g zbar               (values decoded once, Eq. 6)
+    A sequence of length 0 gives out = 0. Returns float64 [B, n_q, d_h]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, d_h = q.shape
+    out = np.zeros((B, n_q, d_h), dtype=np.float64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T == 0:
+            continue
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G))        # [T, G]
+        for h in range(n_q):
+            Wk, Wv = decoder_blocks(W_kv, _kv_head(h, n_q, n_kv), n_kv, d_h)
+            qt = Wk.T @ q[b, h]
+            s = (Z @ qt) / math.sqrt(d_h)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            zbar = Z.T @ p
+            out[b, h] = Wv @ zbar
+    return out
+
+
+def decode_attn_materialised(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
+    """The same step with keys and values written out, Eq. 5 without N_k and
+    RoPE: K = Z W_k,g^T, V = Z W_v,g^T, then textbook softmax(K q / sqrt(d_h))^T V."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, d_h = q.shape
+    out = np.zeros((B, n_q, d_h), dtype=np.float64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T == 0:
+            continue
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G))
+        for h in range(n_q):
+            Wk, Wv = decoder_blocks(W_kv, _kv_head(h, n_q, n_kv), n_kv, d_h)
+            K = Z @ Wk.T
+            V = Z @ Wv.T
+            s = K @ q[b, h] / math.sqrt(d_h)
+            w = np.exp(s - s.max())
+            w /= w.sum()
+            out[b, h] = w @ V
+    return out
+
+
+def decode_partials(q, packed, W_kv, seq_lens, n_kv: int, G: int, bounds):
+    """Split form of decode_attn over token ranges [bounds[i], bounds[i+1]).
+
+    Returns per split (m, l, acc) with m = max s, l = sum exp(s - m),
+    acc = sum exp(s - m) z, each per (b, h), and the merged output
+      M = max m_i, zbar = sum_i e^(m_i - M) acc_i / sum_i e^(m_i - M) l_i,
+      out = W_v,g zbar.
+    This is the "merge partials" step of the slides' kernel frame; it must equal
+    decode_attn for any split points (a test checks that)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, d_h = q.shape
+    out = np.zeros((B, n_q, d_h), dtype=np.float64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T == 0:
+            continue
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G))
+        for h in range(n_q):
+            Wk, Wv = decoder_blocks(W_kv, _kv_head(h, n_q, n_kv), n_kv, d_h)
+            qt = Wk.T @ q[b, h]
+            parts = []
+            for lo, hi in zip(bounds[:-1], bounds[1:]):
+                lo, hi = min(lo, T), min(hi, T)
+                if hi <= lo:
+                    continue
+                s = Z[lo:hi] @ qt / math.sqrt(d_h)
+                m = s.max()
+                e = np.exp(s - m)
+                parts.append((m, e.sum(), Z[lo:hi].T @ e))
+            M = max(m for m, _, _ in parts)
+            l = sum(math.exp(m - M) * li for m, li, _ in parts)
+            acc = sum(math.exp(m - M) * a for m, _, a in parts)
+            out[b, h] = Wv @ (acc / l)
+    return out

@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs shared by the oracle-side tests, the GPU tests and the bench.
+
+This module draws random numbers and lays them out in the input formats the
+library consumes (bf16 bit patterns, packed code bytes, int32 lengths). It holds
+none of the method's arithmetic: no projection, no quantiser, no packing of
+codes from levels, no attention. Both the oracle and the HIP path receive the
+same arrays from here and compute everything else on their own.
+
+Seeds: every tensor comes from ``numpy.random.Generator(PCG64(SeedSequence(
+[workload_id, layer, tensor_id])))`` so that any tensor of any layer can be
+regenerated in isolation (the bench and the tests draw the same bytes).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+# tensor ids inside a (workload, layer) seed
+T_X = 1          # residual states x for the append
+T_E = 2          # encoder E
+T_WKV = 3        # shared decoder W_kv
+T_Q = 4          # decode queries q
+T_CODES = 5      # uniform cache code bytes
+T_LENS = 6       # ragged sequence lengths
+T_XNEW = 7       # the one new residual state appended per decode step
+
+
+def rng(workload_id: int, layer: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, layer, tensor_id])))
+
+
+# ---------------------------------------------------------------- bf16 formats
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns as uint16. Inputs here are finite normals."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact: every bfloat16 value is a float64 value."""
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def normal_bf16(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) drawn in float32, rounded to bf16, returned as uint16 bits."""
+    return f32_to_bf16_bits(g.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+# ----------------------------------------------------------- code-byte inputs
+def bytes_per_token(G: int) -> int:
+    """Storage width of one token's codes at 4 bits per coordinate."""
+    return (G * 4 + 7) // 8
+
+
+def uniform_code_bytes(g: np.random.Generator, shape_tokens, G: int) -> np.ndarray:
+    """Random cache bytes whose nibbles are i.i.d. uniform codes in 0..15.
+
+    Two 4-bit codes share a byte, so uniform codes are uniform bytes. For odd G
+    the unused high nibble of each token's last byte is zero (the storage
+    convention of the packed cache)."""
+    P = bytes_per_token(G)
+    shape = tuple(np.atleast_1d(shape_tokens)) + (P,)
+    out = g.integers(0, 256, size=shape, dtype=np.uint8)
+    if G % 2:
+        out[..., -1] &= 0x0F
+    return out
+
+
+def loguniform_lengths(g: np.random.Generator, batch: int, lo: int, hi: int) -> np.ndarray:
+    """floor(exp(U[ln lo, ln hi))) as int32."""
+    v = np.floor(np.exp(g.uniform(math.log(lo), math.log(hi), size=batch))).astype(np.int64)
+    return np.clip(v, lo, hi).astype(np.int32)
+
+
+# ---------------------------------------------------------------- workloads
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shapes of one synthetic workload (Qwen3-shaped attention layers)."""
+    wid: int
+    name: str
+    layers: int
+    C: int
+    n_q: int
+    n_kv: int
+    d_h: int
+    G: int
+    batch: int
+    context: int            # tokens per sequence (max for ragged)
+    ragged: bool = False
+    append_tokens: int = 0  # prefill chunk appended through E + FSQ (0 = none)
+    codes_from_fsq: bool = False
+
+    @property
+    def P(self) -> int:
+        return bytes_per_token(self.G)
+
+
+WORKLOADS = {
+    "tiny": Workload(0, "tiny", 1, 1024, 16, 8, 128, 64, 1, 1024, append_tokens=1024),
+    "qwen3_8b_g256": Workload(1, "qwen3_8b_g256", 36, 4096, 32, 8, 128, 256, 1, 32768),
+    "qwen3_8b_g84": Workload(2, "qwen3_8b_g84", 36, 4096, 32, 8, 128, 84, 1, 131072,
+                             append_tokens=8192),
+    "qwen3_1p7b_ragged": Workload(3, "qwen3_1p7b_ragged", 28, 2048, 16, 8, 128, 256, 16, 65536,
+                                  ragged=True),
+    "qwen3_8b_g84_1m": Workload(4, "qwen3_8b_g84_1m", 36, 4096, 32, 8, 128, 84, 1, 1048576,
+                                codes_from_fsq=True),
+}
+
+
+def seq_lens(w: Workload, layer: int = 0) -> np.ndarray:
+    if w.ragged:
+        # one set of lengths per workload (shared by all layers of a step)
+        return loguniform_lengths(rng(w.wid, 0, T_LENS), w.batch, 4096, w.context)
+    return np.full(w.batch, w.context, dtype=np.int32)
+
+
+def layer_weights(w: Workload, layer: int):
+    """E [G, C] ~ N(0, 1/C) and W_kv [2 n_kv d_h, G] ~ N(0, 1/G), bf16 bits."""
+    E = normal_bf16(rng(w.wid, layer, T_E), (w.G, w.C), 1.0 / math.sqrt(w.C))
+    W_kv = normal_bf16(rng(w.wid, layer, T_WKV), (2 * w.n_kv * w.d_h, w.G), 1.0 / math.sqrt(w.G))
+    return E, W_kv
+
+
+def layer_query(w: Workload, layer: int) -> np.ndarray:
+    return normal_bf16(rng(w.wid, layer, T_Q), (w.batch, w.n_q, w.d_h), 1.0)
+
+
+def layer_x(w: Workload, layer: int, n_tokens: int, tensor_id: int = T_X) -> np.ndarray:
+    return normal_bf16(rng(w.wid, layer, tensor_id), (n_tokens, w.C), 1.0)
+
+
+def layer_codes(w: Workload, layer: int, lens: np.ndarray | None = None, cap: int | None = None) -> np.ndarray:
+    """Uniform cache bytes [batch, cap, P]; rows at t >= seq_lens[b] are zero."""
+    cap = w.context if cap is None else cap
+    out = uniform_code_bytes(rng(w.wid, layer, T_CODES), (w.batch, cap), w.G)
+    if lens is not None:
+        for b, T in enumerate(lens):
+            out[b, int(T):] = 0
+    return out
