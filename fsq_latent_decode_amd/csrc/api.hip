@@ -1,0 +1,68 @@
+// C ABI of the library (declared in include/fsq.h): validation, workspace
+// sizing and launches on the caller's stream. No device memory is allocated here.
+#include "../../include/fsq.h"
+#include "common.h"
+#include "decode_plan.h"
+
+namespace fsq {
+hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
+                         int G, hipStream_t st);
+hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
+                         const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
+                         int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
+                         hipStream_t st);
+}  // namespace fsq
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+const char *fsq_status_string(int status) {
+    switch (status) {
+        case FSQ_OK: return "FSQ_OK";
+        case FSQ_ERR_NULL: return "FSQ_ERR_NULL";
+        case FSQ_ERR_SHAPE: return "FSQ_ERR_SHAPE";
+        case FSQ_ERR_UNSUPPORTED: return "FSQ_ERR_UNSUPPORTED";
+        case FSQ_ERR_WORKSPACE: return "FSQ_ERR_WORKSPACE";
+        case FSQ_ERR_HIP: return "FSQ_ERR_HIP";
+        default: return "FSQ_UNKNOWN";
+    }
+}
+
+int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_tokens, int32_t C,
+               int32_t G, void *stream) {
+    if (n_tokens < 0 || C < 1 || G < 1) return FSQ_ERR_SHAPE;
+    if (G > FSQ_MAX_G || C % 8 != 0) return FSQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return FSQ_OK;
+    if (!x || !E || !codes) return FSQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(E)) return FSQ_ERR_UNSUPPORTED;
+    if (n_tokens > ((int64_t)1 << 31) * 32) return FSQ_ERR_UNSUPPORTED;
+    hipError_t e = fsq::launch_append(x, E, codes, n_tokens, C, G, (hipStream_t)stream);
+    return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
+}
+
+size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap) {
+    if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return 0;
+    return fsq::make_decode_plan(batch, n_q, G, seq_cap).total;
+}
+
+int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                    const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                    int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
+    if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
+    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > fsq::kMaxDh) return FSQ_ERR_UNSUPPORTED;
+    if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
+    if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
+    if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
+    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
+    if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u))
+        return FSQ_ERR_WORKSPACE;
+    if ((int64_t)pl.S > 65535 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
+    hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
+                                      seq_cap, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
+}
+
+}  // extern "C"

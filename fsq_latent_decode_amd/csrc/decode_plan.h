@@ -1,0 +1,46 @@
+// Split-K plan and workspace layout of the decode call. Pure host arithmetic:
+// the plan depends only on the call's sizes, so the workspace size can be
+// queried without a device.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fsq {
+
+constexpr int kMaxG = 256;     // largest latent width the decode kernels are built for
+constexpr int kMaxDh = 256;    // largest head dimension
+constexpr int kMaxNq = 64;     // largest number of query heads
+constexpr int kTargetCtas = 512;   // split-K CTAs aimed for per call (about 2 per CU)
+constexpr int kMinChunk = 256;     // fewest tokens per split
+constexpr int kChunkQuantum = 128; // chunk granularity (4 waves x 32-token tiles)
+
+struct DecodePlan {
+    int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
+    int nqp = 0;      // n_q padded to a multiple of 32 (head groups)
+    int chunk = 0;    // tokens per split
+    int S = 0;        // splits per sequence (0 when seq_cap == 0)
+    size_t off_qt = 0, off_acc = 0, off_ml = 0, total = 0;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
+    DecodePlan p;
+    p.GP = (G + 31) / 32 * 32;
+    p.nqp = (n_q + 31) / 32 * 32;
+    int64_t per = (int64_t(batch) * seq_cap + kTargetCtas - 1) / kTargetCtas;
+    if (per < kMinChunk) per = kMinChunk;
+    per = (per + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+    if (per > (int64_t)1 << 30) per = (int64_t)1 << 30;
+    p.chunk = (int)per;
+    p.S = (int)((seq_cap + p.chunk - 1) / p.chunk);
+    const int S1 = p.S > 0 ? p.S : 1;
+    p.off_qt = 0;
+    p.off_acc = align256((size_t)batch * p.nqp * p.GP * 2);
+    p.off_ml = p.off_acc + align256((size_t)batch * S1 * n_q * p.GP * 4);
+    p.total = p.off_ml + align256((size_t)batch * S1 * n_q * 2 * 4);
+    return p;
+}
+
+}  // namespace fsq

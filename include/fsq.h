@@ -1,0 +1,135 @@
+/*
+ * fsq.h - C ABI of the Transformer-FSQ latent-decode library for AMD MI355X (gfx950).
+ *
+ * The cache stores, per token and layer, G four-bit finite-scalar-quantised
+ * codes of z = FSQ(E x) and nothing else. Keys and values exist only through a
+ * shared decoder W_kv = [W_k; W_v]. Definitions are those of the pages
+ * "Transformer-FSQ: Discrete Latents for Extreme KV-Cache Compression"
+ * (picx.dev summary: Eq. 2 quantiser, Eq. 4 encoder, Eq. 5-6 keys/values and
+ * values decoded after pooling; Byte Budgeting) and the slides "Transformer-FSQ"
+ * (frame "A wide product code uses four bits per coordinate": L = 16, h = 7.5075,
+ * delta = 0.5, ceil(G b / 8) bytes per token per layer; frame "The kernel reads
+ * codes and never writes reconstructed K/V": the decode kernel's steps).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates no device memory, keeps no pointer after returning, and holds
+ *     no per-call state; calls on different streams may run concurrently as
+ *     long as they use distinct output and workspace buffers.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
+ *     enqueue work on it and return; nothing synchronises with the host. A
+ *     device-side fault surfaces at the caller's next synchronisation.
+ *   - Arguments are validated before any HIP call. On a validation failure
+ *     nothing is enqueued and no output is touched.
+ *   - Returns an fsq_status; fsq_status_string() names it. No C++ exception
+ *     crosses this interface.
+ *
+ * Code layout (a reading of the pages, which fix only the byte count):
+ *   level  = round-half-even(h * tanh(u + atanh(delta / h)) - delta) in -8..7,
+ *   code   = level + 8 in 0..15,
+ *   byte j of a token = code[2j] | (code[2j+1] << 4), j < ceil(G/2); for odd G
+ *   the last high nibble is zero. A token row is exactly ceil(G/2) bytes; rows
+ *   of one sequence are contiguous.
+ */
+#ifndef FSQ_H
+#define FSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fsq_status {
+    FSQ_OK = 0,
+    FSQ_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    FSQ_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or  */
+                             /* the sizes are inconsistent (n_q % n_kv != 0, ...)  */
+    FSQ_ERR_UNSUPPORTED = 3, /* valid but outside what the kernels implement       */
+    FSQ_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required            */
+    FSQ_ERR_HIP = 5          /* a HIP runtime call (device query, launch) failed   */
+} fsq_status;
+
+/* Static name of a status code ("FSQ_OK", ...; "FSQ_UNKNOWN" otherwise). */
+const char *fsq_status_string(int status);
+
+/* Limits enforced by validation. */
+#define FSQ_MAX_G 256          /* latent width G: 1..FSQ_MAX_G                       */
+#define FSQ_MAX_NQ 64          /* query heads per sequence: 1..FSQ_MAX_NQ            */
+#define FSQ_MAX_DH 256         /* head dimension d_h: 1..FSQ_MAX_DH                  */
+
+/*
+ * fsq_append - encode residual states and write their packed codes.
+ *
+ * Computes z_t = Q_FSQ(E x_t) (Eq. 4 with the Eq. 2 forward value) for each of
+ * the n_tokens rows of x and stores the packed codes.
+ *   x      [n_tokens, C]        bf16, row-major, 16-byte aligned.
+ *   E      [G, C]               bf16, row-major (the encoder), 16-byte aligned.
+ *   codes  [n_tokens, ceil(G/2)] u8 destination rows (the caller points at the
+ *                               first row to write, e.g. cache + T * ceil(G/2));
+ *                               any byte alignment is accepted.
+ *   n_tokens >= 0 (0 enqueues nothing), C >= 1 with C % 8 == 0, 1 <= G <= FSQ_MAX_G.
+ * Arithmetic: bf16 products accumulated in fp32 (MFMA for n_tokens >= 32,
+ * vector FMA below), bound and round in fp32. Compared with an exact fp64
+ * evaluation a code can differ by +-1 only where u~ lies within fp32 rounding
+ * of a half-integer.
+ * Errors: FSQ_ERR_NULL (x, E or codes NULL with n_tokens > 0),
+ *         FSQ_ERR_SHAPE (n_tokens < 0, C < 1, G < 1), FSQ_ERR_UNSUPPORTED
+ *         (C % 8 != 0, G > FSQ_MAX_G, x or E not 16-byte aligned), FSQ_ERR_HIP.
+ */
+int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes,
+               int64_t n_tokens, int32_t C, int32_t G, void *stream);
+
+/*
+ * fsq_decode_workspace_bytes - device workspace that fsq_decode_attn needs for
+ * these sizes (the absorbed queries and the split-K partial states).
+ * Returns 0 for invalid sizes. Depends only on its arguments.
+ */
+size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap);
+
+/*
+ * fsq_decode_attn - one decode step of attention read from the packed cache.
+ *
+ * For each sequence b and query head h (kv head g = h / (n_q / n_kv)), over
+ * the cached positions t < seq_lens[b]:
+ *   q~   = (log2(e) / sqrt(d_h)) * W_k,g^T q[b,h]        (query absorbed into latent space)
+ *   s_t  = q~ . z_t,  z_t = code_t - 8                   (scores, log2 domain)
+ *   zbar = sum_t 2^(s_t - max s) z_t / sum_t 2^(s_t - max s)   (codes pooled, Eq. 6)
+ *   out[b,h] = W_v,g zbar                                 (values decoded once, Eq. 6)
+ * i.e. softmax(K q / sqrt(d_h))^T V with K = Z W_k,g^T and V = Z W_v,g^T (Eq. 5
+ * without key norm and RoPE). Keys and values are never written to memory.
+ *   q        [batch, n_q, d_h]              bf16.
+ *   codes    [batch, seq_cap, ceil(G/2)]    u8 packed cache (layout above),
+ *                                           16-byte aligned.
+ *   W_kv     [2 * n_kv * d_h, G]            bf16; rows [0, n_kv d_h) are W_k and
+ *                                           rows [n_kv d_h, 2 n_kv d_h) are W_v,
+ *                                           each kv-head-major (d_h rows per head).
+ *   seq_lens [batch]                        int32 on the device; values are
+ *                                           clamped to [0, seq_cap]. A length of
+ *                                           0 yields out[b] = 0.
+ *   out      [batch, n_q, d_h]              bf16 (written).
+ *   workspace, workspace_bytes              device scratch of at least
+ *                                           fsq_decode_workspace_bytes(...) bytes,
+ *                                           256-byte aligned; its content on entry
+ *                                           is irrelevant and it is overwritten.
+ * Sizes: batch >= 1, 1 <= n_q <= FSQ_MAX_NQ, n_kv >= 1, n_q % n_kv == 0,
+ *        1 <= d_h <= FSQ_MAX_DH, 1 <= G <= FSQ_MAX_G, seq_cap >= 0.
+ * Arithmetic: fp16 MFMA operands (levels are exact in fp16; q~ rounded to
+ * fp16 after scaling), fp32 accumulation and softmax, bf16 output.
+ * Errors: FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED (d_h, G, n_q limits,
+ *         codes not 16-byte aligned),
+ *         FSQ_ERR_WORKSPACE (NULL, too small or misaligned), FSQ_ERR_HIP.
+ */
+int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                    const int32_t *seq_lens, uint16_t *out,
+                    int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                    int64_t seq_cap, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSQ_H */

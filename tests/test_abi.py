@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fsq.h declares, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fsq_latent_decode_amd as fsq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsq.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(fsq.library_path()),
+                               reason="libfsq.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(fsq.EXPORTS)
+
+
+def test_header_compiles_as_c(tmp_path):
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "t.c"
+    src.write_text('#include "fsq.h"\nint main(void){return FSQ_OK;}\n')
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c",
+                        str(src), "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(fsq.library_path())
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+@needs_lib
+def test_status_strings():
+    assert fsq.status_string(0) == "FSQ_OK"
+    assert fsq.status_string(fsq.FSQ_ERR_WORKSPACE) == "FSQ_ERR_WORKSPACE"
+    assert fsq.status_string(99) == "FSQ_UNKNOWN"
+
+
+@needs_lib
+def test_workspace_bytes_host_logic():
+    L = fsq.lib()
+    assert L.fsq_decode_workspace_bytes(0, 32, 256, 10) == 0
+    assert L.fsq_decode_workspace_bytes(1, 65, 256, 10) == 0
+    assert L.fsq_decode_workspace_bytes(1, 32, 257, 10) == 0
+    assert L.fsq_decode_workspace_bytes(1, 32, 256, -1) == 0
+    small = L.fsq_decode_workspace_bytes(1, 32, 256, 1024)
+    big = L.fsq_decode_workspace_bytes(1, 32, 256, 32768)
+    assert 0 < small <= big
+    # holds at least the absorbed queries (fp16) and one split of partials (fp32)
+    assert small >= 32 * 256 * 2 + 32 * 256 * 4 + 32 * 2 * 4
+    assert L.fsq_decode_workspace_bytes(1, 32, 84, 0) > 0
+    assert L.fsq_decode_workspace_bytes(1, 32, 84, 1 << 20) % 256 == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    # (q, codes, W, lens, out, batch, n_q, n_kv, d_h, G, cap, ws, ws_bytes)
+    ((1, 1, 1, 1, 1, 0, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((1, 1, 1, 1, 1, 1, 32, 6, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((1, 1, 1, 1, 1, 1, 32, 8, 128, 256, -1, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((1, 1, 1, 1, 1, 1, 32, 8, 512, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((1, 1, 1, 1, 1, 1, 32, 8, 128, 300, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((1, 1, 1, 1, 1, 1, 128, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((0, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 0, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 8, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 0, 1 << 20), fsq.FSQ_ERR_WORKSPACE),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 64), fsq.FSQ_ERR_WORKSPACE),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 128, 1 << 20), fsq.FSQ_ERR_WORKSPACE),
+])
+def test_decode_validation_before_any_hip_call(args, status):
+    # pointer values are never dereferenced: every case fails validation first
+    (q, c, w, l, o, B, nq, nkv, dh, G, cap, ws, wsb) = args
+    rc = fsq.lib().fsq_decode_attn(q, c, w, l, o, B, nq, nkv, dh, G, cap, ws, wsb, None)
+    assert rc == status
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    ((256, 256, 256, -1, 64, 8), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 4, 0, 8), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 4, 64, 0), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 4, 60, 8), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 4, 64, 257), fsq.FSQ_ERR_UNSUPPORTED),
+    ((0, 256, 256, 4, 64, 8), fsq.FSQ_ERR_NULL),
+    ((256, 256, 0, 4, 64, 8), fsq.FSQ_ERR_NULL),
+    ((264, 256, 256, 4, 64, 8), fsq.FSQ_ERR_UNSUPPORTED),
+    ((0, 0, 0, 0, 64, 8), fsq.FSQ_OK),
+])
+def test_append_validation_before_any_hip_call(args, status):
+    x, E, c, n, C, G = args
+    assert fsq.lib().fsq_append(x, E, c, n, C, G, None) == status
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(fsq, "_lib", None)
+    monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        fsq.lib()

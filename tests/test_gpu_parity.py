@@ -1,0 +1,225 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on seeded inputs.
+
+Bars (the workload's stated tolerances):
+  * codes: bit-exact except that at most 1e-4 of them may differ, each by +-1,
+    and only where the oracle's bounded value u~ lies within TIE_TOL of a
+    half-integer (an fp32 rounding tie; TIE_TOL is derived in the design notes
+    from the fp32 accumulation error of E x);
+  * attention output: relative L2 error <= 5e-3 per call (fp32 accumulation,
+    fp16 operands, bf16 output).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import fsq_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+FLIP_RATE = 1e-4
+TIE_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def fsq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fsq_latent_decode_amd as m
+    m.lib()          # fails loudly if the library is missing
+    return m
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def check_codes(gpu_packed, x_bits, E_bits, G):
+    """Compare GPU codes with the oracle's under the tie rule; return flip count."""
+    x = synth.bf16_bits_to_f64(x_bits)
+    E = synth.bf16_bits_to_f64(E_bits)
+    u = orc.projection(x, E)
+    ref = orc.fsq_codes(u)
+    got = orc.unpack_codes(gpu_packed, G)
+    # the unused high nibble of an odd-G token must be zero
+    if G % 2:
+        assert np.all(gpu_packed[:, -1] >> 4 == 0)
+    diff = got.astype(int) - ref.astype(int)
+    bad = np.nonzero(diff)
+    n_bad = len(bad[0])
+    assert np.all(np.abs(diff) <= 1), "a code differs by more than 1"
+    assert n_bad <= max(1, int(FLIP_RATE * ref.size)), f"{n_bad} flipped codes"
+    if n_bad:
+        ut = orc.fsq_bound(u[bad])
+        dist = np.abs(ut - (np.floor(ut) + 0.5))
+        assert np.all(dist < TIE_TOL), f"flip away from a tie: {dist.max()}"
+    return n_bad
+
+
+def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0):
+    n, C = x_bits.shape
+    G = E_bits.shape[0]
+    P = orc.bytes_per_token(G)
+    rows = n if dest_rows is None else dest_rows
+    cache = torch.full((rows, P), 0xAB, dtype=torch.uint8, device="cuda")
+    fsq.fsq_append(dev_bf16(x_bits), dev_bf16(E_bits), cache[row0:row0 + n])
+    torch.cuda.synchronize()
+    return cache.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,C,G", [
+    (1, 1024, 64), (5, 512, 83), (17, 256, 7), (31, 4096, 84),     # vector path
+    (32, 1024, 64), (33, 1024, 64), (100, 520, 84), (1024, 1024, 64),  # MFMA path, ragged tails
+    (257, 2048, 256), (64, 8, 3), (96, 24, 1),
+])
+def test_append_parity(fsq, n, C, G):
+    g = synth.rng(100, n, C + G)
+    x = synth.normal_bf16(g, (n, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    got = run_append(fsq, x, E)
+    check_codes(got, x, E, G)
+
+
+def test_append_into_cache_rows_keeps_other_rows(fsq):
+    g = synth.rng(101, 0, 0)
+    x = synth.normal_bf16(g, (40, 256))
+    E = synth.normal_bf16(g, (84, 256), 1 / 16)
+    got = run_append(fsq, x, E, dest_rows=50, row0=3)          # row offset 3*42: 2-byte aligned
+    assert np.all(got[:3] == 0xAB) and np.all(got[43:] == 0xAB)
+    check_codes(got[3:43], x, E, 84)
+    got1 = run_append(fsq, x[:1], E, dest_rows=5, row0=3)       # one-token (decode-step) append
+    assert np.all(got1[:3] == 0xAB) and np.all(got1[4:] == 0xAB)
+    check_codes(got1[3:4], x[:1], E, 84)
+
+
+def test_append_prefill_chunk_g84(fsq):
+    """The 8192-token prefill chunk of the G=84 Qwen3-8B workload, full size."""
+    w = synth.WORKLOADS["qwen3_8b_g84"]
+    E, _ = synth.layer_weights(w, 0)
+    x = synth.layer_x(w, 0, w.append_tokens)
+    got = run_append(fsq, x, E)
+    flips = check_codes(got, x, E, w.G)
+    print(f"g84 prefill chunk: {flips} of {x.shape[0] * w.G} codes at fp32 ties")
+
+
+# ------------------------------------------------------------------ decode
+def run_decode(fsq, q_bits, packed, W_bits, lens, n_kv, workspace=None):
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn(q, dev_u8(packed), dev_bf16(W_bits),
+                        torch.from_numpy(np.asarray(lens, np.int32)).cuda(), out, n_kv,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_decode(q_bits, packed, W_bits, lens, n_kv, G):
+    q = synth.bf16_bits_to_f64(q_bits)
+    W = synth.bf16_bits_to_f64(W_bits)
+    return orc.decode_attn(q, packed, W, lens, n_kv, G)
+
+
+def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
+    g = synth.rng(200, seed, 0)
+    q = synth.normal_bf16(g, (B, n_q, d_h))
+    W = synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G))
+    packed = synth.uniform_code_bytes(g, (B, cap), G)
+    return q, packed, W, np.asarray(lens, np.int32)
+
+
+@pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens", [
+    (1, 16, 8, 128, 64, 1024, [1024]),          # the tiny single-layer workload shape
+    (1, 32, 8, 128, 256, 1, [1]),
+    (1, 32, 8, 128, 256, 33, [33]),
+    (1, 32, 8, 128, 84, 700, [700]),
+    (2, 32, 8, 128, 84, 1000, [1000, 257]),
+    (4, 16, 8, 128, 256, 600, [0, 1, 31, 600]),
+    (1, 64, 8, 128, 64, 300, [300]),             # two 32-head groups
+    (1, 8, 1, 64, 37, 130, [129]),               # MQA, odd G, d_h 64
+    (3, 12, 4, 96, 96, 2100, [2100, 1500, 33]),
+    (1, 32, 8, 128, 160, 5000, [4999]),
+])
+def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
+    q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
+    got = run_decode(fsq, q, packed, W, lens, n_kv)
+    ref = oracle_decode(q, packed, W, lens, n_kv, G)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            e = rel_l2(got[b], ref[b])
+            assert e < REL_L2, (b, e)
+
+
+def test_decode_deterministic_and_split_invariant(fsq):
+    q, packed, W, lens = decode_case(5, 2, 32, 8, 128, 84, 9000, [9000, 4097])
+    a = run_decode(fsq, q, packed, W, lens, 8)
+    b = run_decode(fsq, q, packed, W, lens, 8)
+    assert np.array_equal(a, b)
+    ref = oracle_decode(q, packed, W, lens, 8, 84)
+    assert rel_l2(a, ref) < REL_L2
+
+
+def test_decode_workspace_too_small_raises(fsq):
+    q, packed, W, lens = decode_case(6, 1, 32, 8, 128, 64, 100, [100])
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fsq.FsqError, match="WORKSPACE"):
+        run_decode(fsq, q, packed, W, lens, 8, workspace=ws)
+
+
+def test_tiny_workload_append_then_decode(fsq):
+    """The tiny workload end to end: append the 1024-token context, then decode
+    one query, compared with the oracle's encode-then-decode."""
+    w = synth.WORKLOADS["tiny"]
+    E, W = synth.layer_weights(w, 0)
+    x = synth.layer_x(w, 0, w.append_tokens)
+    q = synth.layer_query(w, 0)
+    got_codes = run_append(fsq, x, E)
+    check_codes(got_codes, x, E, w.G)
+    out = torch.empty((1, w.n_q, w.d_h), dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn(dev_bf16(q), dev_u8(got_codes[None]), dev_bf16(W),
+                        torch.tensor([w.context], dtype=torch.int32, device="cuda"), out, w.n_kv)
+    torch.cuda.synchronize()
+    ref_codes = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x), synth.bf16_bits_to_f64(E)))
+    ref = oracle_decode(q, ref_codes[None], W, [w.context], w.n_kv, w.G)
+    assert rel_l2(out.float().cpu().numpy(), ref) < REL_L2
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_g256", "qwen3_8b_g84"])
+def test_decode_full_size_layer(fsq, name):
+    """One layer of the Qwen3-8B-shaped workloads at full context (layers 0 and last)."""
+    w = synth.WORKLOADS[name]
+    for layer in (0, w.layers - 1):
+        _, W = synth.layer_weights(w, layer)
+        q = synth.layer_query(w, layer)
+        lens = synth.seq_lens(w)
+        packed = synth.layer_codes(w, layer)
+        got = run_decode(fsq, q, packed, W, lens, w.n_kv)
+        ref = oracle_decode(q, packed, W, lens, w.n_kv, w.G)
+        e = rel_l2(got, ref)
+        print(f"{name} layer {layer}: rel L2 {e:.2e}")
+        assert e < REL_L2
+
+
+def test_decode_ragged_batch_full_size(fsq):
+    """The ragged Qwen3-1.7B-shaped batch (16 sequences, 4096..65536 tokens), layer 0."""
+    w = synth.WORKLOADS["qwen3_1p7b_ragged"]
+    _, W = synth.layer_weights(w, 0)
+    q = synth.layer_query(w, 0)
+    lens = synth.seq_lens(w)
+    packed = synth.layer_codes(w, 0, lens=lens)
+    got = run_decode(fsq, q, packed, W, lens, w.n_kv)
+    ref = oracle_decode(q, packed, W, lens, w.n_kv, w.G)
+    for b in range(w.batch):
+        assert rel_l2(got[b], ref[b]) < REL_L2, b
