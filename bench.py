@@ -1,0 +1,322 @@
+"""Decode-step throughput of the FSQ latent-decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode step of a whole model: for each layer, the new token's
+residual state is appended (E projection, FSQ, packing: fsq_append) and the
+query attends over the packed cache (fsq_decode_attn). Inputs are seeded
+synthetic tensors of the workload's shapes, resident in HBM before timing.
+Each step is replayed from a HIP graph; steps rotate over enough replicas of
+the per-layer buffers that one step's data is never still in the 256 MB
+Infinity Cache from its previous use.
+
+Prints one JSON line: context-tokens/s (sum of sequence lengths / step time),
+the step's roofline fraction, the split-K kernel's roofline (HIP events from
+hipExtLaunchKernelGGL around each launch, in a second phase of eager steps), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_g256", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--also", default="qwen3_8b_g84",
+                    help="comma-separated extra workloads reported under 'also' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
+    ap.add_argument("--timing-steps", type=int, default=5,
+                    help="eager steps whose split-K launches are bracketed by HIP events")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device copy of this size (counter calibration) and exit")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- arithmetic
+def decode_call_bytes(w, lens):
+    codes = int(np.sum(lens)) * w.P
+    wkv = 2 * w.n_kv * w.d_h * w.G * 2
+    qo = 2 * w.batch * w.n_q * w.d_h * 2 + 4 * w.batch
+    return codes + wkv + qo
+
+
+def append_call_bytes(w):
+    return w.G * w.C * 2 + w.batch * w.C * 2 + w.batch * w.P
+
+
+def step_flops(w, lens):
+    T = float(np.sum(lens))
+    lat = 4.0 * w.n_q * w.G * T                       # scores + pooling
+    per_seq = 4.0 * w.n_q * w.d_h * w.G * w.batch     # absorb + W_v
+    app = 2.0 * w.batch * w.G * w.C
+    return w.layers * (lat + per_seq + app)
+
+
+# --------------------------------------------------------------- GPU side
+class Model:
+    """Per-layer device buffers of one replica of the workload."""
+
+    def __init__(self, w, torch, replicas):
+        import fsq_latent_decode_amd as fsq
+        self.fsq, self.torch, self.w = fsq, torch, w
+        dev = "cuda"
+        self.lens_np = synth.seq_lens(w)
+        self.cap = w.context
+        self.lens = torch.from_numpy(self.lens_np).to(dev)
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        base = []
+        for l in range(w.layers):
+            E, W = synth.layer_weights(w, l)
+            codes = synth.layer_codes(w, l, lens=self.lens_np if w.ragged else None)
+            base.append(dict(E=bf(E), W=bf(W), q=bf(synth.layer_query(w, l)),
+                             x=bf(synth.layer_x(w, l, w.batch, synth.T_XNEW)),
+                             codes=torch.from_numpy(codes).to(dev)))
+        self.reps = [base]
+        for _ in range(replicas - 1):
+            self.reps.append([{k: v.clone() for k, v in d.items()} for d in base])
+        for rep in self.reps:
+            for d in rep:
+                d["out"] = torch.empty((w.batch, w.n_q, w.d_h), dtype=torch.bfloat16, device=dev)
+        self.ws = fsq.alloc_workspace(w.batch, w.n_q, w.G, self.cap, dev)
+        torch.cuda.synchronize()
+
+    def step(self, r, ev=None):
+        """One decode step over replica r; ev[l] = (start, stop) events bracket
+        layer l's split-K kernel (eager calls only)."""
+        fsq, w = self.fsq, self.w
+        for l, d in enumerate(self.reps[r]):
+            for b in range(w.batch):
+                T = int(self.lens_np[b])
+                fsq.fsq_append(d["x"][b:b + 1], d["E"], d["codes"][b, T - 1:T])
+            fsq.fsq_decode_attn(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv,
+                                workspace=self.ws, split_events=None if ev is None else ev[l])
+
+
+def run_workload(w, torch, steps, warmup, eager, timing_steps):
+    per_step_bytes = w.layers * (decode_call_bytes(w, synth.seq_lens(w)) + append_call_bytes(w))
+    replicas = max(2, math.ceil(4 * MALL_BYTES / per_step_bytes))
+    replicas = min(replicas, 8)
+    m = Model(w, torch, replicas)
+    graphs = None
+    if not eager:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for r in range(replicas):     # warm the library and the allocator outside capture
+                m.step(r)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                m.step(r)
+            graphs.append(g)
+
+    def run(i):
+        r = i % replicas
+        if graphs is not None:
+            graphs[r].replay()
+        else:
+            m.step(r)
+
+    # phase A: throughput of whole steps (graph replays, inputs resident in HBM)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        run(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+
+    # phase B: eager steps with HIP events around every split-K kernel launch
+    call_ms = []
+    for i in range(timing_steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(w.layers)]
+        m.step((warmup + steps + i) % replicas, ev)
+        torch.cuda.synchronize()
+        call_ms.extend(a.elapsed_time(b) for a, b in ev)
+    return m, ms, call_ms, replicas
+
+
+def copy_probe(torch, mib):
+    n = mib * 2 ** 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 3}))
+
+
+# --------------------------------------------------------------- CPU side
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (oracle/) as it stands, on a bounded sample of the step:
+    whole layers (one-token append + decode at full context), extrapolated to
+    the workload's layer count."""
+    from oracle import fsq_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    lens = synth.seq_lens(w)
+    done, t_total = 0, 0.0
+    l = 0
+    while t_total < seconds and done < w.layers:
+        E, W = synth.layer_weights(w, l)
+        x = synth.bf16_bits_to_f64(synth.layer_x(w, l, w.batch, synth.T_XNEW))
+        q = synth.bf16_bits_to_f64(synth.layer_query(w, l))
+        packed = synth.layer_codes(w, l, lens=lens if w.ragged else None)
+        Wf = synth.bf16_bits_to_f64(W)
+        Ef = synth.bf16_bits_to_f64(E)
+        t = time.perf_counter()
+        new = orc.pack_codes(orc.encode(x, Ef))
+        for b in range(w.batch):
+            packed[b, int(lens[b]) - 1] = new[b]
+        orc.decode_attn(q, packed, Wf, lens, w.n_kv, w.G)
+        t_total += time.perf_counter() - t
+        done += 1
+        l += 1
+    per_step = t_total / done * w.layers
+    return {"value": float(np.sum(lens)) / per_step, "unit": "context-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {w.layers} layers (one-token append + decode at full context), "
+                      f"{t_total:.1f} s, extrapolated x{w.layers / done:.1f} to one step",
+            "step_s": per_step}
+
+
+def split_kernel_bytes(w, lens):
+    """Algorithmic bytes of one split-K launch: the layer's packed codes."""
+    return int(np.sum(lens)) * w.P
+
+
+def traffic_from_profile(w):
+    """HBM bytes per split-K launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_split_traffic_{w.name}.txt")
+    src = os.path.join(ROOT, "fsq_latent_decode_amd", "csrc", "decode.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if kv.get("decode_hip_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(w, ms, call_ms, replicas):
+    lens = synth.seq_lens(w)
+    ctx = float(np.sum(lens))
+    step_bytes = w.layers * (decode_call_bytes(w, lens) + append_call_bytes(w))
+    t_bytes = step_bytes / (HBM_PEAK_GBS * 1e9)
+    t_flops = step_flops(w, lens) / (MFMA_FP16_PEAK_TFLOPS * 1e12)
+    t_roof = max(t_bytes, t_flops)
+    res = {"value": ctx / (ms * 1e-3), "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+           "step_roofline": {"bytes": step_bytes, "flops": step_flops(w, lens),
+                             "t_roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3)},
+           "replicas": replicas}
+    if call_ms:
+        avg = float(np.mean(call_ms))
+        nbytes = split_kernel_bytes(w, lens)
+        ach = nbytes / (avg * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic_from_profile(w),
+                           "kernel": "decode_split_kernel", "bytes_per_launch": nbytes,
+                           "avg_launch_us": avg * 1e3, "launches_timed": len(call_ms),
+                           "timing": "hipExtLaunchKernelGGL start/stop events, eager steps"}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
+        return
+    w = synth.WORKLOADS[args.workload]
+    m, ms, call_ms, reps = run_workload(w, torch, args.steps, args.warmup, args.eager,
+                                        args.timing_steps)
+    main_res = summarize(w, ms, call_ms, reps)
+    del m
+    torch.cuda.empty_cache()
+    also = {}
+    for name in [s for s in args.also.split(",") if s and s != args.workload]:
+        w2 = synth.WORKLOADS[name]
+        m2, ms2, cm2, reps2 = run_workload(w2, torch, max(5, args.steps // 2), args.warmup,
+                                           args.eager, args.timing_steps)
+        also[name] = summarize(w2, ms2, cm2, reps2)
+        del m2
+        torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    line = {
+        "metric": "decode context-tokens/s",
+        "value": main_res["value"],
+        "unit": "context-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
+                   "context": int(np.max(synth.seq_lens(w))), "G": w.G, "C": w.C, "n_q": w.n_q,
+                   "n_kv": w.n_kv, "d_h": w.d_h, "bytes_per_token_per_layer": w.P,
+                   "step": "per layer: fsq_append of the new token + fsq_decode_attn"},
+        "decode_steps_per_s": main_res["steps_per_s"],
+        "step_roofline": main_res["step_roofline"],
+        "roofline": main_res.get("roofline"),
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -14,7 +14,8 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
-EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn")
+EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
+           "fsq_decode_attn_timed")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_workspace_bytes.restype = sz
         L.fsq_decode_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, vp, sz, vp]
         L.fsq_decode_attn.restype = ctypes.c_int
+        L.fsq_decode_attn_timed.argtypes = L.fsq_decode_attn.argtypes + [vp, vp]
+        L.fsq_decode_attn_timed.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -116,11 +119,13 @@ def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -
 
 def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, seq_lens: torch.Tensor,
                     out: torch.Tensor, n_kv: int, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, split_events=None) -> torch.Tensor:
     """One decode step of attention over the packed cache; writes and returns out.
 
     q [B, n_q, d_h] bf16, codes [B, cap, ceil(G/2)] uint8, W_kv [2 n_kv d_h, G] bf16,
-    seq_lens [B] int32 (device), out [B, n_q, d_h] bf16."""
+    seq_lens [B] int32 (device), out [B, n_q, d_h] bf16. With split_events =
+    (start, stop) (torch.cuda.Event with timing) the call goes through
+    fsq_decode_attn_timed and the events bracket the split-K kernel."""
     _dev(q, "q", torch.bfloat16, 3)
     _dev(codes, "codes", torch.uint8, 3)
     _dev(W_kv, "W_kv", torch.bfloat16, 2)
@@ -138,8 +143,18 @@ def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, se
     if workspace is None:
         workspace = alloc_workspace(B, n_q, G, cap, q.device)
     _dev(workspace, "workspace", torch.uint8, 1)
-    rc = lib().fsq_decode_attn(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(),
-                               out.data_ptr(), B, n_q, n_kv, d_h, G, cap, workspace.data_ptr(),
-                               workspace.numel(), _stream(stream))
-    _check(rc, "fsq_decode_attn")
+    args = (q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+            B, n_q, n_kv, d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if split_events is None:
+        _check(lib().fsq_decode_attn(*args), "fsq_decode_attn")
+    else:
+        ev = [_event_handle(e) for e in split_events]
+        _check(lib().fsq_decode_attn_timed(*args, ev[0], ev[1]), "fsq_decode_attn_timed")
     return out
+
+
+def _event_handle(ev) -> int:
+    """The hipEvent_t behind a torch.cuda.Event (created on first record)."""
+    if ev.cuda_event == 0:          # torch creates the event lazily
+        ev.record()
+    return ev.cuda_event

@@ -10,7 +10,7 @@ hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, i
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                          const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
-                         hipStream_t st);
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 }  // namespace fsq
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -46,13 +46,13 @@ size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t
     return fsq::make_decode_plan(batch, n_q, G, seq_cap).total;
 }
 
-int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
-                    const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
-                    int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                         const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                         int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                         size_t workspace_bytes, void *stream, void *ev0, void *ev1) {
     if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
-    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > fsq::kMaxDh) return FSQ_ERR_UNSUPPORTED;
+    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH) return FSQ_ERR_UNSUPPORTED;
     if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
     if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
     if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
@@ -61,8 +61,27 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
         return FSQ_ERR_WORKSPACE;
     if ((int64_t)pl.S > 65535 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
-                                      seq_cap, workspace, (hipStream_t)stream);
+                                      seq_cap, workspace, (hipStream_t)stream, (hipEvent_t)ev0,
+                                      (hipEvent_t)ev1);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
+}
+
+int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                    const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                    int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                         workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                          size_t workspace_bytes, void *stream, void *split_start,
+                          void *split_stop) {
+    if (!split_start || !split_stop) return FSQ_ERR_NULL;
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                         workspace, workspace_bytes, stream, split_start, split_stop);
 }
 
 }  // extern "C"

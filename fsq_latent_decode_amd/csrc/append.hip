@@ -26,26 +26,29 @@ __device__ inline float dot8_bf16(u32x4 a, u32x4 b) {
     return s;
 }
 
+template <int NT>
 __global__ __launch_bounds__(256) void append_gemv_kernel(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ E,
                                                           uint8_t *__restrict__ codes, int n, int C,
                                                           int G, float shift) {
-    __shared__ float red[kAppendWaves][kGemvTokens][2];
-    const int j = blockIdx.x;                 // output byte = coordinates 2j, 2j+1
-    const int tb = blockIdx.y * kGemvTokens;  // first token of this CTA
-    const int nt = (n - tb) < kGemvTokens ? (n - tb) : kGemvTokens;
+    __shared__ float red[kAppendWaves][NT][2];
+    const int j = blockIdx.x;            // output byte = coordinates 2j, 2j+1
+    const int tb = blockIdx.y * NT;      // first token of this CTA
+    const int nt = (n - tb) < NT ? (n - tb) : NT;
     const int c0 = 2 * j, c1 = 2 * j + 1;
     const bool has1 = c1 < G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float acc[kGemvTokens][2];
+    float acc[NT][2];
 #pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t) acc[t][0] = acc[t][1] = 0.0f;
+    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = 0.0f;
     const int nv = C / 8;
+    const u32x4 *e0p = reinterpret_cast<const u32x4 *>(E + (size_t)c0 * C);
+    const u32x4 *e1p = reinterpret_cast<const u32x4 *>(E + (size_t)(has1 ? c1 : c0) * C);
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        const u32x4 e0 = reinterpret_cast<const u32x4 *>(E + (size_t)c0 * C)[v];
-        const u32x4 e1 = has1 ? reinterpret_cast<const u32x4 *>(E + (size_t)c1 * C)[v] : u32x4{};
+        const u32x4 e0 = e0p[v];
+        const u32x4 e1 = has1 ? e1p[v] : u32x4{};
 #pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) {
+        for (int t = 0; t < NT; ++t) {
             if (t < nt) {
                 const u32x4 xv = reinterpret_cast<const u32x4 *>(x + (size_t)(tb + t) * C)[v];
                 acc[t][0] += dot8_bf16(e0, xv);
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void append_gemv_kernel(const uint16_t *__rest
         }
     }
 #pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             float a = acc[t][c];
@@ -143,8 +146,15 @@ hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, i
                          int G, hipStream_t st) {
     const float shift = (float)atanh((double)kDelta / (double)kH);
     if (n < 32) {
-        dim3 grid(bytes_per_token(G), (unsigned)((n + kGemvTokens - 1) / kGemvTokens));
-        append_gemv_kernel<<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift);
+        const int nt = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : kGemvTokens;
+        dim3 grid(bytes_per_token(G), (unsigned)((n + nt - 1) / nt));
+        switch (nt) {
+            case 1: append_gemv_kernel<1><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
+            case 2: append_gemv_kernel<2><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
+            case 4: append_gemv_kernel<4><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
+            default:
+                append_gemv_kernel<kGemvTokens><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift);
+        }
         return hipGetLastError();
     }
     const int GP = (G + 31) / 32 * 32;

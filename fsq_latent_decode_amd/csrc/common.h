@@ -40,16 +40,18 @@ __device__ inline uint32_t fsq_code(float u, float shift) {
     return (uint32_t)((int)lv + kCodeOffset);
 }
 
-// Position of latent coordinate k inside the fp16 operand order used by the
-// decode kernel: each group of 8 coordinates (one packed dword) is unpacked as
-// the fp16 pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7).
-__host__ __device__ inline int coord_to_pos(int k) {
-    const int e = k & 7;
-    return (k & ~7) | ((e & 3) << 1) | (e >> 2);
+// Position of latent coordinate k inside the fp16 operand order of the decode
+// kernel (GP = G padded to a multiple of 32, KB = GP / 16 score k-blocks).
+// Packed dword D of a token (coordinates 8D..8D+7) feeds k-block D % KB from
+// lane half D / KB, so each half reads one contiguous run of dwords; inside a
+// dword the fp16 pairs are (c0,c4) (c1,c5) (c2,c6) (c3,c7).
+__host__ __device__ inline int coord_to_pos(int k, int GP) {
+    const int KB = GP / 16, D = k >> 3, e = k & 7;
+    return 16 * (D % KB) + 8 * (D / KB) + (((e & 3) << 1) | (e >> 2));
 }
-__host__ __device__ inline int pos_to_coord(int p) {
-    const int j = p & 7;
-    return (p & ~7) | ((j & 1) << 2) | (j >> 1);
+__host__ __device__ inline int pos_to_coord(int p, int GP) {
+    const int KB = GP / 16, kb = p >> 4, hh = (p >> 3) & 1, j = p & 7;
+    return 8 * (kb + hh * KB) + (((j & 1) << 2) | (j >> 1));
 }
 
 }  // namespace fsq

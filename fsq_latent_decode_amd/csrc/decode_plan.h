@@ -12,7 +12,10 @@ constexpr int kMaxG = 256;     // largest latent width the decode kernels are bu
 constexpr int kMaxDh = 256;    // largest head dimension
 constexpr int kMaxNq = 64;     // largest number of query heads
 constexpr int kTargetCtas = 512;   // split-K CTAs aimed for per call (about 2 per CU)
-constexpr int kMinChunk = 256;     // fewest tokens per split
+#ifndef FSQ_MIN_CHUNK
+#define FSQ_MIN_CHUNK 256
+#endif
+constexpr int kMinChunk = FSQ_MIN_CHUNK;   // fewest tokens per split
 constexpr int kChunkQuantum = 128; // chunk granularity (4 waves x 32-token tiles)
 
 struct DecodePlan {
@@ -38,7 +41,7 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
     const int S1 = p.S > 0 ? p.S : 1;
     p.off_qt = 0;
     p.off_acc = align256((size_t)batch * p.nqp * p.GP * 2);
-    p.off_ml = p.off_acc + align256((size_t)batch * S1 * n_q * p.GP * 4);
+    p.off_ml = p.off_acc + align256((size_t)batch * S1 * n_q * p.GP * 2);   // fp16 zbar
     p.total = p.off_ml + align256((size_t)batch * S1 * n_q * 2 * 4);
     return p;
 }

@@ -128,6 +128,20 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
                     int64_t seq_cap, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * fsq_decode_attn_timed - fsq_decode_attn that also records two caller-created
+ * hipEvent_t (passed as void *) around the split-K kernel, the call's dominant
+ * kernel, using hipExtLaunchKernelGGL: split_start when that kernel starts and
+ * split_stop when it completes. For measurement; the results are identical to
+ * fsq_decode_attn. Not for use under stream capture.
+ * Errors: as fsq_decode_attn; FSQ_ERR_NULL if an event is NULL.
+ */
+int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                          const int32_t *seq_lens, uint16_t *out,
+                          int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                          int64_t seq_cap, void *workspace, size_t workspace_bytes,
+                          void *stream, void *split_start, void *split_stop);
+
 #ifdef __cplusplus
 }
 #endif
