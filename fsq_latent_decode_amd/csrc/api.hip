@@ -59,7 +59,8 @@ static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t
     const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
     if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u))
         return FSQ_ERR_WORKSPACE;
-    if ((int64_t)pl.S > 65535 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
+    // the merge kernel reduces at most 1024 splits (the plan gives <= 512 / batch + 1)
+    if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
                                       seq_cap, workspace, (hipStream_t)stream, (hipEvent_t)ev0,
                                       (hipEvent_t)ev1);

@@ -24,8 +24,8 @@
 
 namespace fsq {
 
-constexpr int kTile = 32;     // tokens per wave iteration (the score MFMA's M)
-constexpr int kWaves = 4;     // waves per CTA, each on its own token tiles
+constexpr int kTile = 32;        // tokens per wave and round (the score MFMA's M)
+constexpr int kWaves = 4;        // waves per CTA of the absorb and merge kernels
 
 // fp16 levels of one packed dword (8 codes, nibble i = coordinate 8D + i), in
 // the operand order (c0,c4)(c1,c5)(c2,c6)(c3,c7): 0x6400 | n is the fp16 value
@@ -47,67 +47,108 @@ __device__ inline half8 unpack_levels(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- absorb
-// q~[b, h, pos(k)] = scale * sum_d W_k[g d_h + d, k] q[b, h, d] for the grp heads
-// h of kv head g. One CTA per (kv head, 64 latent columns, sequence); the 256
-// threads are 64 columns x 4 quarters of d, each thread holding its W_k values
-// in registers while it forms the grp dot products.
+// q~[b, h, pos(k)] = scale * sum_d W_k[g d_h + d, k] q[b, h, d] for the heads h
+// of kv head g. One CTA per (kv head, 64 latent columns, sequence). A thread
+// holds VW adjacent columns (one VW x bf16 load per row) for the rows
+// d = dg, dg + DG, ...; the DG row groups are summed through LDS.
 constexpr int kAbsorbCols = 64;
-constexpr int kMergeWvElems = 128 * 272;   // LDS for W_v blocks up to 128 padded rows of 256
-constexpr int kAbsorbHeadBatch = 8;
+constexpr int kAbsorbHeads = 4;    // heads reduced per LDS pass
 
+template <int VW>
+struct AbsorbCfg {
+    static constexpr int CG = kAbsorbCols / VW;   // column groups per CTA
+    static constexpr int DG = 256 / CG;           // row groups
+    static constexpr int RMAX = kMaxDh / DG;      // rows per thread at most
+};
+
+template <int VW> struct VecT;
+template <> struct VecT<8> { typedef u32x4 T; };
+template <> struct VecT<4> { typedef uint2 T; };
+template <> struct VecT<2> { typedef uint32_t T; };
+template <> struct VecT<1> { typedef uint16_t T; };
+
+template <int VW>
+__device__ inline void bf16_vec_to_f32(const typename VecT<VW>::T &v, float *f) {
+    if constexpr (VW == 1) {
+        f[0] = __uint_as_float((uint32_t)v << 16);
+    } else {
+        const uint32_t *u = reinterpret_cast<const uint32_t *>(&v);
+#pragma unroll
+        for (int i = 0; i < VW / 2; ++i) {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <int VW>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict__ q,
                                                      const uint16_t *__restrict__ W_kv,
                                                      _Float16 *__restrict__ qt, int G, int GP,
                                                      int n_q, int nqp, int n_kv, int d_h,
                                                      float scale) {
-    extern __shared__ float qs[];   // [grp][d_h]
-    __shared__ float red[4][kAbsorbHeadBatch][kAbsorbCols];
+    using A = AbsorbCfg<VW>;
+    using VT = typename VecT<VW>::T;
+    __shared__ float qs[kAbsorbHeads][kMaxDh];
+    __shared__ float red[A::DG][kAbsorbHeads][kAbsorbCols];
     const int g = blockIdx.x, b = blockIdx.z;
-    const int col = threadIdx.x & (kAbsorbCols - 1), qd = threadIdx.x >> 6;
-    const int k = blockIdx.y * kAbsorbCols + col;
+    const int tid = threadIdx.x, cg = tid % A::CG, dg = tid / A::CG;
+    const int k0 = blockIdx.y * kAbsorbCols + cg * VW;
+    const bool kin = k0 < G;                  // G % VW == 0: the group is all in or all out
     const int grp = n_q / n_kv;
-    for (int i = threadIdx.x; i < grp * d_h; i += blockDim.x)
-        qs[i] = bf16_to_f32(q[((size_t)b * n_q + (size_t)g * grp) * d_h + i]);
-    // rows past n_q up to the 32-head padding are zero (written once, by kv head 0)
-    if (g == 0 && k < GP && qd == 0)
-        for (int h = n_q; h < nqp; ++h) qt[((size_t)b * nqp + h) * GP + k] = (_Float16)0.0f;
-    __syncthreads();
-    const int dq = (d_h + 3) / 4;
-    const int d0 = qd * dq, d1 = (d0 + dq < d_h) ? d0 + dq : d_h;
-    float w[kMaxDh / 4];
-    const bool kin = k < G;
-    // every load is issued unconditionally from a clamped (valid) address so that
-    // all of them are in flight together; out-of-range values are zeroed after
-    const int kc = kin ? k : G - 1;
-    const uint16_t *wcol = W_kv + (size_t)g * d_h * G + kc;
-    uint16_t wr[kMaxDh / 4];
+    // W_k rows of this thread: loads issued unconditionally from clamped addresses
+    const uint16_t *wk = W_kv + (size_t)g * d_h * G + (kin ? k0 : 0);
+    VT wr[A::RMAX];
 #pragma unroll
-    for (int i = 0; i < kMaxDh / 4; ++i) {
-        const int d = (d0 + i < d_h) ? d0 + i : d_h - 1;
-        wr[i] = wcol[(size_t)d * G];
+    for (int i = 0; i < A::RMAX; ++i) {
+        const int d = dg + A::DG * i;
+        wr[i] = *reinterpret_cast<const VT *>(wk + (size_t)(d < d_h ? d : d_h - 1) * G);
     }
+    // rows past n_q up to the 32-head padding are zero (written once, by kv head 0)
+    if (g == 0 && dg == 0)
+        for (int c = 0; c < VW; ++c)
+            if (k0 + c < GP)
+                for (int h = n_q; h < nqp; ++h) qt[((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
+    float w[A::RMAX][VW];
 #pragma unroll
-    for (int i = 0; i < kMaxDh / 4; ++i) w[i] = (kin && d0 + i < d1) ? bf16_to_f32(wr[i]) : 0.0f;
-    for (int hb = 0; hb < grp; hb += kAbsorbHeadBatch) {
-        const int nh = (grp - hb) < kAbsorbHeadBatch ? (grp - hb) : kAbsorbHeadBatch;
-        for (int j = 0; j < nh; ++j) {
-            // w[i] is zero past this thread's d range; the clamped q index keeps
-            // the LDS reads in range without a per-element branch
-            const float *qj = qs + (hb + j) * d_h;
-            float a0 = 0.0f, a1 = 0.0f;
+    for (int i = 0; i < A::RMAX; ++i) {
+        bf16_vec_to_f32<VW>(wr[i], w[i]);
+        const bool ok = kin && dg + A::DG * i < d_h;
 #pragma unroll
-            for (int i = 0; i < kMaxDh / 4; i += 2) {
-                a0 += w[i] * qj[(d0 + i) < d_h ? d0 + i : d_h - 1];
-                a1 += w[i + 1] * qj[(d0 + i + 1) < d_h ? d0 + i + 1 : d_h - 1];
-            }
-            red[qd][j][col] = a0 + a1;
+        for (int c = 0; c < VW; ++c) w[i][c] = ok ? w[i][c] : 0.0f;
+    }
+    for (int hb = 0; hb < grp; hb += kAbsorbHeads) {
+        const int nh = (grp - hb) < kAbsorbHeads ? (grp - hb) : kAbsorbHeads;
+        for (int i = tid; i < kAbsorbHeads * kMaxDh; i += blockDim.x) {
+            const int j = i / kMaxDh, d = i - j * kMaxDh;
+            qs[j][d] = (j < nh && d < d_h)
+                           ? bf16_to_f32(q[((size_t)b * n_q + (size_t)g * grp + hb + j) * d_h + d])
+                           : 0.0f;
         }
         __syncthreads();
-        if (qd == 0 && k < GP) {
-            for (int j = 0; j < nh; ++j) {
-                const float a = red[0][j][col] + red[1][j][col] + red[2][j][col] + red[3][j][col];
+        for (int j = 0; j < nh; ++j) {
+            float a[VW];
+#pragma unroll
+            for (int c = 0; c < VW; ++c) a[c] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < A::RMAX; ++i) {
+                const int d = dg + A::DG * i;
+                const float qv = qs[j][d < kMaxDh ? d : kMaxDh - 1];
+#pragma unroll
+                for (int c = 0; c < VW; ++c) a[c] += w[i][c] * qv;
+            }
+#pragma unroll
+            for (int c = 0; c < VW; ++c) red[dg][j][cg * VW + c] = a[c];
+        }
+        __syncthreads();
+        for (int o = tid; o < nh * kAbsorbCols; o += blockDim.x) {
+            const int j = o / kAbsorbCols, col = o - j * kAbsorbCols;
+            const int k = blockIdx.y * kAbsorbCols + col;
+            if (k < GP) {
+                float sum = 0.0f;
+                for (int r = 0; r < A::DG; ++r) sum += red[r][j][col];
                 const int h = g * grp + hb + j;
-                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP)] = (_Float16)(kin ? a * scale : 0.0f);
+                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP)] = (_Float16)(k < G ? sum * scale : 0.0f);
             }
         }
         __syncthreads();
@@ -115,24 +156,24 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
 }
 
 // ----------------------------------------------------------------- split
-// One CTA = 4 waves working through its token chunk in rounds of 4 x 32 tokens.
+// One CTA = NW waves (8 or 4) working through its token chunk in rounds of
+// NW x 32 tokens.
 // In a round each wave loads (one round ahead, straight into registers),
 // unpacks and scores its own 32-token tile against all 32 heads; the waves then
 // agree on a per-head reference max and normaliser through LDS, and every wave
 // pools all 4 tiles but only for its own latent coordinate blocks (block cb
-// belongs to wave cb % 4). The softmax state is therefore identical in all
+// belongs to wave cb % NW). The softmax state is therefore identical in all
 // waves and the pooled sums need no cross-wave combine.
-template <int GP>
+template <int GP, int NW>
 struct SplitCfg {
     static constexpr int KB = GP / 16;                 // score k-blocks = dwords per lane half
     static constexpr int CB = GP / 32;                 // pooling coordinate blocks
-    static constexpr int CBW = (CB + kWaves - 1) / kWaves;   // blocks per wave
+    static constexpr int CBW = (CB + NW - 1) / NW;   // blocks per wave
     static constexpr int RS = (GP / 2 + 63) / 64 * 64; // dwords per fp16 tile row
     static constexpr int kTileDw = kTile * RS;
-    static constexpr int kZBytes = kWaves * kTileDw * 4;
-    static constexpr int kPBytes = kWaves * 2 * 64 * 16;
-    static constexpr int kCbufBytes = 32 * (GP + 1) * 4;
-    static_assert(kCbufBytes <= kZBytes, "epilogue buffer must fit in the tile region");
+    static constexpr int kZBytes = NW * kTileDw * 4;
+    static constexpr int kPBytes = NW * 2 * 64 * 16;
+    static_assert(32 * (GP + 8) * 2 <= kZBytes, "Q~ staging must fit in the tile region");
 };
 
 // XOR swizzle (dword granularity) of the fp16 tile: the 16-byte row writes of
@@ -140,12 +181,12 @@ struct SplitCfg {
 // both fall on distinct LDS banks.
 __device__ inline int zt_swz(int row) { return 16 * (row & 3) + 4 * ((row >> 2) & 3); }
 
-template <int GP, bool AL>
-__global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
+template <int GP, int NW, bool AL>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
     float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S) {
-    using C = SplitCfg<GP>;
+    using C = SplitCfg<GP, NW>;
     constexpr int KB = C::KB, CB = C::CB, CBW = C::CBW, RS = C::RS;
     constexpr int NLD = AL ? KB : KB + 1;   // dwords loaded per lane per tile
     // the reference max may lag the true max by this much (log2 units) before the
@@ -153,7 +194,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
     constexpr float kRescaleSlack = 8.0f;
     __shared__ __attribute__((aligned(16))) uint32_t zsm[C::kZBytes / 4];
     __shared__ __attribute__((aligned(16))) uint8_t psm[C::kPBytes];
-    __shared__ float tmax_s[kWaves][32], tsum_s[kWaves][32];
+    __shared__ float tmax_s[NW][32], tsum_s[NW][32];
 
     const int P = (G + 1) / 2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -197,11 +238,24 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
 
     issue(c0 + wave * kTile);
 
+    // Q~ rows of this head group (32 x GP fp16, contiguous) are read from global
+    // once per CTA into LDS (rows padded to GP + 8 halves for conflict-free
+    // 16-byte reads), then each wave takes its B operands from there
     half8 qv[KB];
     {
-        const _Float16 *qrow = qt + ((size_t)b * nqp + hg * 32 + t) * GP + hh * 8;
+        constexpr int QROW = GP + 8;
+        _Float16 *qsm = reinterpret_cast<_Float16 *>(zsm);   // the tile region is free here
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
+        constexpr int NQ16 = 32 * GP / 8;                    // 16-byte chunks
+        for (int i = threadIdx.x; i < NQ16; i += NW * 64) {
+            const int r = i / (GP / 8), c = i - r * (GP / 8);
+            *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qsrc[i];
+        }
+        __syncthreads();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) qv[kb] = *reinterpret_cast<const half8 *>(qrow + 16 * kb);
+        for (int kb = 0; kb < KB; ++kb)
+            qv[kb] = *reinterpret_cast<const half8 *>(qsm + t * QROW + 16 * kb + 8 * hh);
+        __syncthreads();   // before the tile region is reused
     }
 
     float m_ref = -INFINITY, l_run = 0.0f;
@@ -215,7 +269,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
     typedef __attribute__((address_space(3))) shortx4 lds_s4;
     typedef short short8 __attribute__((ext_vector_type(8)));
 
-    for (int64_t r0 = c0; r0 < c1; r0 += kWaves * kTile) {
+    for (int64_t r0 = c0; r0 < c1; r0 += NW * kTile) {
         // ---- phase 1: own tile -> levels -> fp16 tile + scores
         uint32_t cur[KB];
         const int ntok = ld_ntok;
@@ -228,7 +282,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
             for (int i = 0; i < KB; ++i)
                 cur[i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
         }
-        issue(r0 + kWaves * kTile + wave * kTile);
+        issue(r0 + NW * kTile + wave * kTile);
 
         const bool live = t < ntok;
         floatx16 sc0 = floatx16{}, sc1 = floatx16{};
@@ -263,7 +317,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
         // ---- phase 2: common reference max (lazy), probabilities, row sums
         float rmax = tmax_s[0][t];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) rmax = fmaxf(rmax, tmax_s[w][t]);
+        for (int w = 1; w < NW; ++w) rmax = fmaxf(rmax, tmax_s[w][t]);
         const bool bump = rmax > m_ref + kRescaleSlack;
         const float m_new = bump ? rmax : m_ref;
         const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
@@ -288,64 +342,77 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
         __syncthreads();
         float rsum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) rsum += tsum_s[w][t];
+        for (int w = 0; w < NW; ++w) rsum += tsum_s[w][t];
         l_run = l_run * alpha + rsum;
         if (__any(rescale)) {
 #pragma unroll
             for (int j = 0; j < CBW; ++j) acc[j] *= alpha;
         }
 
-        // ---- phase 3: pool the round's tiles for this wave's coordinate blocks
+        // ---- phase 3: pool the round's tiles for this wave's coordinate blocks.
+        // Block cb = wave + 4 j; when CB is a multiple of 4 every wave owns CBW
+        // blocks (known at compile time), otherwise ownership is wave-uniform.
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) {
+        for (int w2 = 0; w2 < NW; ++w2) {
             if (r0 + w2 * kTile >= c1) break;     // empty tile (uniform)
             const uint32_t *zt = zsm + w2 * C::kTileDw;
+            half8 pb[2];
+            shortx4 za[2][CBW][2];
+            // all LDS operand reads of this tile first, then the MFMAs; block
+            // ownership depends only on the (scalar) wave index
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const half8 pb = *reinterpret_cast<const half8 *>(psm + ((w2 * 2 + ks) * 64 + lane) * 16);
+                pb[ks] = *reinterpret_cast<const half8 *>(psm + ((w2 * 2 + ks) * 64 + lane) * 16);
                 const int ra = ks * 16 + hh * 4 + mrow, rb = ra + 8;
 #pragma unroll
                 for (int j = 0; j < CBW; ++j) {
-                    const int cb = wave + kWaves * j;
-                    if (cb < CB) {
+                    const int cb = wv + NW * j;
+                    if (CB % NW == 0 || cb < CB) {
                         const int cdw = cb * 16 + g16 * 8 + pcol * 2;
-                        const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        za[ks][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (lds_s4 *)(zt + ra * RS + (cdw ^ zt_swz(ra))));
-                        const shortx4 a2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        za[ks][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (lds_s4 *)(zt + rb * RS + (cdw ^ zt_swz(rb))));
-                        const short8 zs = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, zs),
-                                                                        pb, acc[j], 0, 0, 0);
                     }
                 }
             }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) {
+                    if (CB % NW == 0 || wv + NW * j < CB) {
+                        const short8 zs = {za[ks][j][0][0], za[ks][j][0][1], za[ks][j][0][2], za[ks][j][0][3],
+                                           za[ks][j][1][0], za[ks][j][1][1], za[ks][j][1][2], za[ks][j][1][3]};
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, zs), pb[ks],
+                                                                        acc[j], 0, 0, 0);
+                    }
+                }
         }
         __syncthreads();   // the next round overwrites the tiles and probabilities
     }
 
-    // ---- epilogue: zbar = acc / l (operand-position order) via LDS, fp16 out
+    // ---- epilogue: zbar = acc / l in operand-position order, fp16, stored from
+    // registers: each lane holds head t and, per block, 4 runs of 4 positions
     const float invL = 1.0f / l_run;
-    float *cbuf = reinterpret_cast<float *>(zsm);   // [32 heads][GP + 1]
-#pragma unroll
-    for (int j = 0; j < CBW; ++j) {
-        const int cb = wave + kWaves * j;
-        if (cb < CB) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int pos = cb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                cbuf[t * (GP + 1) + pos] = acc[j][r] * invL;
-            }
-        }
-    }
-    __syncthreads();
     const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
     const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    for (int idx = threadIdx.x; idx < heads * (GP / 4); idx += blockDim.x) {
-        const int hd = idx / (GP / 4), p4 = idx - hd * (GP / 4);
-        const float *src = cbuf + hd * (GP + 1) + p4 * 4;
-        const half4 v = {(_Float16)src[0], (_Float16)src[1], (_Float16)src[2], (_Float16)src[3]};
-        *reinterpret_cast<half4 *>(part_z + (pbase + hd) * GP + p4 * 4) = v;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if (t < heads) {
+        _Float16 *dst = part_z + (pbase + t) * GP;
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+            const int cb = wv + NW * j;
+            if (CB % NW == 0 || cb < CB) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const half4 v = {(_Float16)(acc[j][4 * r4 + 0] * invL), (_Float16)(acc[j][4 * r4 + 1] * invL),
+                                     (_Float16)(acc[j][4 * r4 + 2] * invL), (_Float16)(acc[j][4 * r4 + 3] * invL)};
+                    *reinterpret_cast<half4 *>(dst + cb * 32 + r4 * 8 + hh * 4) = v;
+                }
+            }
+        }
     }
     if (wave == 0 && lane < heads) {
         part_ml[(pbase + lane) * 2 + 0] = m_ref;
@@ -355,17 +422,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
 
 // ----------------------------------------------------------------- merge
 // One CTA per (head, sequence): M = max_i m_i, c_i = l_i 2^(m_i - M),
-// zbar = sum_i c_i zbar_i / sum_i c_i, out = W_v,g zbar. The partials are read
-// with 16-byte loads spread over (8-position group x split group) threads.
+// zbar = sum_i c_i zbar_i / sum_i c_i, out = W_v,g zbar. Every global load (the
+// (m, l) pairs, the first 16 partial rows per thread, and this thread's part of
+// its W_v row, VW bf16 per load) is issued before any is used.
+constexpr int kMergeRows = 16;        // partial rows per thread per batch
+constexpr int kMergeMl = 4;           // (m, l) pairs per thread: S <= 1024
+
+template <int VW>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
     int chunk, int S) {
-    extern __shared__ float coef[];   // [S]
+    using VT = typename VecT<VW>::T;
+    constexpr int NVT = kMaxG / VW / 2;   // W_v vectors per thread (two or more threads per row)
+    __shared__ float coef[kMergeMl * 256];
     __shared__ float zpart[256 * 8];   // [split group][GP]
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
-    __shared__ __attribute__((aligned(16))) uint16_t wv_s[kMergeWvElems];
     __shared__ float red[8];
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -377,89 +450,97 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
         for (int d = tid; d < d_h; d += blockDim.x) o[d] = 0;
         return;
     }
-    // stage this kv head's W_v block (d_h x G bf16, contiguous in memory) in LDS
-    // rows of WS dwords; the loads are issued first so that they overlap the
-    // partial-state loads below. TPR threads share an output row; WS / 4 = TPR
-    // (mod 16) puts the 16-byte reads of one pass (16 / TPR rows x TPR chunks)
-    // on distinct banks.
+    const size_t srow = (size_t)n_q;   // rows between splits
+
+    // ---- issue: (m, l) pairs
+    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (size_t)b * S * n_q + h;
+    float2 mlr[kMergeMl];
+#pragma unroll
+    for (int u = 0; u < kMergeMl; ++u) {
+        const int i = tid + 256 * u;
+        mlr[u] = ml[(size_t)(i < ns ? i : ns - 1) * srow];
+    }
+    // ---- issue: first batch of partial rows (thread = 8-position group kg, split group sg)
+    const int KG = GP / 8, SG = 256 / KG;
+    const int kg = tid % KG, sg = tid / KG;
+    const bool zthr = sg < SG;
+    const _Float16 *zp = part_z + ((size_t)b * S * n_q + h) * GP + kg * 8;
+    half8 v[kMergeRows];
+#pragma unroll
+    for (int u = 0; u < kMergeRows; ++u) {
+        const int i = sg + u * SG;
+        v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(zthr && i < ns ? i : 0) * srow * GP);
+    }
+    // ---- issue: W_v row d, vectors part, part + TPR, ... (TPR >= 2 threads per row)
     const int g = h / (n_q / n_kv);
     const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
-    int TPR = 1;
+    int TPR = 2;
     while (TPR * 2 * d_h <= 256 && TPR < 16) TPR *= 2;
-    int WS = ((G + 1) / 2 + 3) / 4 * 4;
-    while (((WS / 4) & 15) != (TPR & 15)) WS += 4;
-    const bool wv_lds = d_h * WS * 2 <= kMergeWvElems;
-    if (wv_lds) {
-        if ((G & 7) == 0 && ((uintptr_t)Wv & 15) == 0) {
-            const int nc = G / 8;
-            for (int i = tid; i < d_h * nc; i += blockDim.x) {
-                const int d = i / nc, c = i - d * nc;
-                *reinterpret_cast<u32x4 *>(wv_s + d * 2 * WS + 8 * c) =
-                    reinterpret_cast<const u32x4 *>(Wv)[i];
-            }
-        } else if ((G & 1) == 0 && ((uintptr_t)Wv & 3) == 0) {
-            const int nc = G / 2;
-            for (int i = tid; i < d_h * nc; i += blockDim.x) {
-                const int d = i / nc, c = i - d * nc;
-                *reinterpret_cast<uint32_t *>(wv_s + d * 2 * WS + 2 * c) =
-                    reinterpret_cast<const uint32_t *>(Wv)[i];
-            }
-        } else {
-            for (int i = tid; i < d_h * G; i += blockDim.x) {
-                const int d = i / G, c = i - d * G;
-                wv_s[d * 2 * WS + c] = Wv[i];
-            }
+    const int NV = G / VW;
+    const bool reg_path = 2 * d_h <= 256;   // every row covered by >= 2 threads in one pass
+    const int d = tid / TPR, part = tid % TPR;
+    const bool drow = reg_path && d < d_h;
+    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
+    VT wv[NVT];
+    if (reg_path) {
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int vi = part + TPR * i;
+            wv[i] = wrow[vi < NV ? vi : NV - 1];
         }
     }
-    const size_t sstride = (size_t)n_q;                       // rows between splits
-    const float *ml = part_ml + ((size_t)b * S * n_q + h) * 2;
+
+    // ---- M and L over all splits (the (m, l) loads are the oldest in flight)
     float M = -INFINITY;
-    for (int i = tid; i < ns; i += blockDim.x) M = fmaxf(M, ml[i * sstride * 2]);
+#pragma unroll
+    for (int u = 0; u < kMergeMl; ++u)
+        if (tid + 256 * u < ns) M = fmaxf(M, mlr[u].x);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     if (lane == 0) red[wave] = M;
     __syncthreads();
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
     float Lp = 0.0f;
-    for (int i = tid; i < ns; i += blockDim.x) {
-        const float c = ml[i * sstride * 2 + 1] * __builtin_amdgcn_exp2f(ml[i * sstride * 2] - M);
-        coef[i] = c;
-        Lp += c;
+#pragma unroll
+    for (int u = 0; u < kMergeMl; ++u) {
+        const int i = tid + 256 * u;
+        if (i < ns) {
+            const float c = mlr[u].y * __builtin_amdgcn_exp2f(mlr[u].x - M);
+            coef[i] = c;
+            Lp += c;
+        }
     }
     for (int off = 32; off > 0; off >>= 1) Lp += __shfl_xor(Lp, off);
-    if (lane == 0) red[wave] = Lp;
+    if (lane == 0) red[4 + wave] = Lp;
     __syncthreads();
-    const float invL = 1.0f / ((red[0] + red[1]) + (red[2] + red[3]));
+    const float invL = 1.0f / ((red[4] + red[5]) + (red[6] + red[7]));
 
-    // zbar in operand-position order: thread = (8-position group kg, split group sg)
-    const int KG = GP / 8, SG = 256 / KG;
-    const int kg = tid % KG, sg = tid / KG;
+    // ---- weighted sum of the partial rows
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (sg < SG) {
-        // up to 16 partial rows per thread in flight at once (indices clamped,
-        // coefficients of the clamped rows zero)
-        constexpr int U = 16;
-        const _Float16 *zp = part_z + ((size_t)b * S * n_q + h) * GP + kg * 8;
-        for (int i0 = sg; i0 < ns; i0 += U * SG) {
-            half8 v[U];
+    if (zthr) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < kMergeRows; ++u) {
+            const int i = sg + u * SG;
+            const float c = i < ns ? coef[i] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] += c * (float)v[u][j];
+        }
+        for (int i0 = sg + kMergeRows * SG; i0 < ns; i0 += kMergeRows * SG) {   // long caches
+#pragma unroll
+            for (int u = 0; u < kMergeRows; ++u) {
                 const int i = i0 + u * SG;
-                v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(i < ns ? i : ns - 1) * sstride * GP);
+                v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(i < ns ? i : ns - 1) * srow * GP);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < kMergeRows; ++u) {
                 const int i = i0 + u * SG;
                 const float c = i < ns ? coef[i] : 0.0f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) a[j] += c * (float)v[u][j];
             }
         }
-    }
-    // reduce over split groups in a fixed order
-    if (sg < SG)
 #pragma unroll
         for (int j = 0; j < 8; ++j) zpart[sg * GP + kg * 8 + j] = a[j];
+    }
     __syncthreads();
     for (int p = tid; p < GP; p += blockDim.x) {
         float z = 0.0f;
@@ -468,46 +549,43 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     }
     __syncthreads();
 
-    // out = W_v,g zbar: TPR threads per output row (from LDS when staged)
-    const int rows_per_pass = 256 / TPR;
-    const int part = tid % TPR;
-    for (int dbase = 0; dbase < d_h; dbase += rows_per_pass) {
-        const int d = dbase + tid / TPR;
+    // ---- out = W_v,g zbar
+    if (reg_path) {
         float acc = 0.0f;
-        if (d < d_h) {
-            if (wv_lds && (G & 7) == 0) {
-                const uint16_t *row = wv_s + d * 2 * WS;
-#pragma unroll 4
-                for (int v = part; v < G / 8; v += TPR) {
-                    const u32x4 wv = *reinterpret_cast<const u32x4 *>(row + 8 * v);
-                    const floatx4 z0 = *reinterpret_cast<const floatx4 *>(zbar + 8 * v);
-                    const floatx4 z1 = *reinterpret_cast<const floatx4 *>(zbar + 8 * v + 4);
-                    acc += __uint_as_float(wv[0] << 16) * z0[0] + __uint_as_float(wv[0] & 0xFFFF0000u) * z0[1];
-                    acc += __uint_as_float(wv[1] << 16) * z0[2] + __uint_as_float(wv[1] & 0xFFFF0000u) * z0[3];
-                    acc += __uint_as_float(wv[2] << 16) * z1[0] + __uint_as_float(wv[2] & 0xFFFF0000u) * z1[1];
-                    acc += __uint_as_float(wv[3] << 16) * z1[2] + __uint_as_float(wv[3] & 0xFFFF0000u) * z1[3];
-                }
-            } else {
-                const uint16_t *row = wv_lds ? wv_s + d * 2 * WS : Wv + (size_t)d * G;
-#pragma unroll 8
-                for (int k = part; k < G; k += TPR) acc += bf16_to_f32(row[k]) * zbar[k];
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int vi = part + TPR * i;
+            float wf[VW];
+            bf16_vec_to_f32<VW>(wv[i], wf);
+            if (vi < NV) {
+#pragma unroll
+                for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
             }
         }
         for (int off = TPR >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (part == 0 && d < d_h) o[d] = f32_to_bf16(acc);
+        if (part == 0 && drow) o[d] = f32_to_bf16(acc);
+    } else {
+        // d_h > 128: one thread per row, loads in the loop
+        for (int dd = tid; dd < d_h; dd += blockDim.x) {
+            float acc = 0.0f;
+            const uint16_t *row = Wv + (size_t)dd * G;
+#pragma unroll 8
+            for (int k = 0; k < G; ++k) acc += bf16_to_f32(row[k]) * zbar[k];
+            o[dd] = f32_to_bf16(acc);
+        }
     }
 }
 
-template <int GP>
-static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
-                               const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
-                               int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
-                               hipEvent_t ev1) {
+template <int GP, int NW>
+static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
+                                  const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
+                                  int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
     dim3 grid(pl.S, batch, pl.nqp / 32);
-    dim3 block(kWaves * 64);
+    dim3 block(NW * 64);
     // whole-dword vector loads when every token row starts on a 16-byte boundary
     const bool al = G == GP && ((G / 2) % 16) == 0 && ((uintptr_t)codes & 15) == 0;
-    auto k = al ? decode_split_kernel<GP, true> : decode_split_kernel<GP, false>;
+    auto k = al ? decode_split_kernel<GP, NW, true> : decode_split_kernel<GP, NW, false>;
     if (ev0 && ev1)   // timed launch: events bracket this kernel's execution
         hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
                               seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S);
@@ -515,6 +593,16 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
         k<<<grid, block, 0, st>>>(qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, pl.nqp, pl.chunk,
                                   pl.S);
     return hipGetLastError();
+}
+
+template <int GP>
+static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
+                               const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
+                               int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
+                               hipEvent_t ev1) {
+    if (pl.waves != split_waves(GP)) return hipErrorInvalidValue;
+    return launch_split_nw<GP, (GP >= 128 ? 8 : 4)>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                    batch, st, ev0, ev1);
 }
 
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
@@ -527,15 +615,23 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
     float *pml = reinterpret_cast<float *>(ws + pl.off_ml);
     const float scale = 1.4426950408889634f / sqrtf((float)d_h);
     hipError_t e;
+    // widest bf16 vector that divides G and the W_kv alignment
+    const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
+                   : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
+                   : ((G & 1) == 0 && ((uintptr_t)W_kv & 3) == 0) ? 2
+                                                                   : 1;
     if (pl.S > 0) {
-        const int grp = n_q / n_kv;
         dim3 ag(n_kv, (pl.GP + kAbsorbCols - 1) / kAbsorbCols, batch);
-        absorb_kernel<<<ag, 256, (size_t)grp * d_h * sizeof(float), st>>>(q, W_kv, qt, G, pl.GP, n_q,
-                                                                         pl.nqp, n_kv, d_h, scale);
+        switch (vw) {
+            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
+            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
+            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
+            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         switch (pl.GP) {
-#define FSQ_SPLIT_CASE(X)                                                                     \
-    case X:                                                                                   \
+#define FSQ_SPLIT_CASE(X)                                                                             \
+    case X:                                                                                           \
         e = launch_split<X>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1); \
         break;
             FSQ_SPLIT_CASE(32)
@@ -552,8 +648,15 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         }
         if (e != hipSuccess) return e;
     }
-    decode_merge_kernel<<<dim3(n_q, batch), 256, (size_t)(pl.S > 0 ? pl.S : 1) * sizeof(float), st>>>(
-        pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S);
+    const dim3 mg(n_q, batch);
+#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S
+    switch (vw) {
+        case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        case 2: decode_merge_kernel<2><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        default: decode_merge_kernel<1><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS);
+    }
+#undef FSQ_MERGE_ARGS
     return hipGetLastError();
 }
 

@@ -11,18 +11,18 @@ namespace fsq {
 constexpr int kMaxG = 256;     // largest latent width the decode kernels are built for
 constexpr int kMaxDh = 256;    // largest head dimension
 constexpr int kMaxNq = 64;     // largest number of query heads
-constexpr int kTargetCtas = 512;   // split-K CTAs aimed for per call (about 2 per CU)
-#ifndef FSQ_MIN_CHUNK
-#define FSQ_MIN_CHUNK 256
-#endif
-constexpr int kMinChunk = FSQ_MIN_CHUNK;   // fewest tokens per split
-constexpr int kChunkQuantum = 128; // chunk granularity (4 waves x 32-token tiles)
+// Split-K CTAs have 8 waves when the padded latent width is >= 128 (their LDS
+// then allows one CTA per CU, so about 256 CTAs are aimed for) and 4 waves
+// below (two or more CTAs per CU, about 512 CTAs). A CTA covers whole rounds of
+// waves x 32 tokens.
+inline int split_waves(int GP) { return GP >= 128 ? 8 : 4; }
 
 struct DecodePlan {
     int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
     int nqp = 0;      // n_q padded to a multiple of 32 (head groups)
     int chunk = 0;    // tokens per split
     int S = 0;        // splits per sequence (0 when seq_cap == 0)
+    int waves = 0;    // waves per split-K CTA
     size_t off_qt = 0, off_acc = 0, off_ml = 0, total = 0;
 };
 
@@ -32,9 +32,12 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
     DecodePlan p;
     p.GP = (G + 31) / 32 * 32;
     p.nqp = (n_q + 31) / 32 * 32;
-    int64_t per = (int64_t(batch) * seq_cap + kTargetCtas - 1) / kTargetCtas;
-    if (per < kMinChunk) per = kMinChunk;
-    per = (per + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+    p.waves = split_waves(p.GP);
+    const int quantum = 32 * p.waves;
+    const int target = p.waves == 8 ? 256 : 512;
+    int64_t per = (int64_t(batch) * seq_cap + target - 1) / target;
+    if (per < quantum) per = quantum;
+    per = (per + quantum - 1) / quantum * quantum;
     if (per > (int64_t)1 << 30) per = (int64_t)1 << 30;
     p.chunk = (int)per;
     p.S = (int)((seq_cap + p.chunk - 1) / p.chunk);

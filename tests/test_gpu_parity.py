@@ -149,6 +149,8 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     (1, 8, 1, 64, 37, 130, [129]),               # MQA, odd G, d_h 64
     (3, 12, 4, 96, 96, 2100, [2100, 1500, 33]),
     (1, 32, 8, 128, 160, 5000, [4999]),
+    (1, 8, 2, 256, 64, 100, [100]),              # d_h 256: one thread per output row
+    (2, 16, 4, 64, 30, 300, [300, 7]),           # G % 4 == 2: 4-byte W_v loads
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -169,6 +171,16 @@ def test_decode_deterministic_and_split_invariant(fsq):
     assert np.array_equal(a, b)
     ref = oracle_decode(q, packed, W, lens, 8, 84)
     assert rel_l2(a, ref) < REL_L2
+
+
+def test_decode_workspace_reuse_across_calls(fsq):
+    """Two calls with different inputs through one workspace: the second result
+    must match the oracle for the second inputs (no stale partial state)."""
+    ws = fsq.alloc_workspace(1, 32, 256, 4096)
+    for seed in (11, 12):
+        q, packed, W, lens = decode_case(seed, 1, 32, 8, 128, 256, 4096, [4096 - seed])
+        got = run_decode(fsq, q, packed, W, lens, 8, workspace=ws)
+        assert rel_l2(got, oracle_decode(q, packed, W, lens, 8, 256)) < REL_L2
 
 
 def test_decode_workspace_too_small_raises(fsq):
