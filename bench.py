@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one decode step of a whole model: for each layer, the new token's
-residual state is appended (E projection, FSQ, packing: fsq_append) and the
-query attends over the packed cache (fsq_decode_attn). Inputs are seeded
+residual state is appended (E projection, FSQ, packing) and the query attends
+over the packed cache, both through one fsq_decode_step call (--two-call:
+fsq_append + fsq_decode_attn, the same kernels plus one launch). Inputs are seeded
 synthetic tensors of the workload's shapes, resident in HBM before timing.
 Each step is replayed from a HIP graph; steps rotate over enough replicas of
 the per-layer buffers that one step's data is never still in the 256 MB
@@ -49,6 +50,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=5,
                     help="eager steps whose split-K launches are bracketed by HIP events")
+    ap.add_argument("--two-call", action="store_true",
+                    help="per layer fsq_append + fsq_decode_attn instead of fsq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a device copy of this size (counter calibration) and exit")
     return ap.parse_args()
@@ -105,11 +108,18 @@ class Model:
         self.ws = fsq.alloc_workspace(w.batch, w.n_q, w.G, self.cap, dev)
         torch.cuda.synchronize()
 
-    def step(self, r, ev=None):
-        """One decode step over replica r; ev[l] = (start, stop) events bracket
-        layer l's split-K kernel (eager calls only)."""
+    def step(self, r, ev=None, two_call=False):
+        """One decode step over replica r: per layer, one fsq_decode_step call
+        (append of the new token at row T - 1 + attention). With ev (eager only),
+        ev[l] = (start, stop) events bracket layer l's split-K kernel; that form
+        issues the same work as fsq_append + fsq_decode_attn_timed (the split-K
+        kernel and its inputs are the same)."""
         fsq, w = self.fsq, self.w
         for l, d in enumerate(self.reps[r]):
+            if ev is None and not two_call:
+                fsq.fsq_decode_step(d["x"], d["E"], d["q"], d["codes"], d["W"], self.lens, d["out"],
+                                    w.n_kv, workspace=self.ws)
+                continue
             for b in range(w.batch):
                 T = int(self.lens_np[b])
                 fsq.fsq_append(d["x"][b:b + 1], d["E"], d["codes"][b, T - 1:T])
@@ -117,7 +127,7 @@ class Model:
                                 workspace=self.ws, split_events=None if ev is None else ev[l])
 
 
-def run_workload(w, torch, steps, warmup, eager, timing_steps):
+def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
     per_step_bytes = w.layers * (decode_call_bytes(w, synth.seq_lens(w)) + append_call_bytes(w))
     replicas = max(2, math.ceil(4 * MALL_BYTES / per_step_bytes))
     replicas = min(replicas, 8)
@@ -128,14 +138,14 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps):
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             for r in range(replicas):     # warm the library and the allocator outside capture
-                m.step(r)
+                m.step(r, two_call=two_call)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
         graphs = []
         for r in range(replicas):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                m.step(r)
+                m.step(r, two_call=two_call)
             graphs.append(g)
 
     def run(i):
@@ -143,7 +153,7 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps):
         if graphs is not None:
             graphs[r].replay()
         else:
-            m.step(r)
+            m.step(r, two_call=two_call)
 
     # phase A: throughput of whole steps (graph replays, inputs resident in HBM)
     for i in range(warmup):
@@ -279,7 +289,7 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     m, ms, call_ms, reps = run_workload(w, torch, args.steps, args.warmup, args.eager,
-                                        args.timing_steps)
+                                        args.timing_steps, args.two_call)
     main_res = summarize(w, ms, call_ms, reps)
     del m
     torch.cuda.empty_cache()
@@ -287,7 +297,7 @@ def main():
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
         w2 = synth.WORKLOADS[name]
         m2, ms2, cm2, reps2 = run_workload(w2, torch, max(5, args.steps // 2), args.warmup,
-                                           args.eager, args.timing_steps)
+                                           args.eager, args.timing_steps, args.two_call)
         also[name] = summarize(w2, ms2, cm2, reps2)
         del m2
         torch.cuda.empty_cache()
@@ -308,7 +318,8 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch,
                    "context": int(np.max(synth.seq_lens(w))), "G": w.G, "C": w.C, "n_q": w.n_q,
                    "n_kv": w.n_kv, "d_h": w.d_h, "bytes_per_token_per_layer": w.P,
-                   "step": "per layer: fsq_append of the new token + fsq_decode_attn"},
+                   "step": ("per layer: fsq_append of the new token + fsq_decode_attn" if args.two_call
+                            else "per layer: fsq_decode_step (append of the new token + attention)")},
         "decode_steps_per_s": main_res["steps_per_s"],
         "step_roofline": main_res["step_roofline"],
         "roofline": main_res.get("roofline"),

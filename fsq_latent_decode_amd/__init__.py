@@ -15,7 +15,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
-           "fsq_decode_attn_timed")
+           "fsq_decode_attn_timed", "fsq_decode_step")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_attn.restype = ctypes.c_int
         L.fsq_decode_attn_timed.argtypes = L.fsq_decode_attn.argtypes + [vp, vp]
         L.fsq_decode_attn_timed.restype = ctypes.c_int
+        L.fsq_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                      vp, sz, vp]
+        L.fsq_decode_step.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -117,6 +120,48 @@ def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv):
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(codes, "codes", torch.uint8, 3)
+    _dev(W_kv, "W_kv", torch.bfloat16, 2)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(out, "out", torch.bfloat16, 3)
+    B, n_q, d_h = q.shape
+    G = W_kv.shape[1]
+    if codes.shape[0] != B or codes.shape[2] != bytes_per_token(G):
+        raise ValueError(f"codes must be [{B}, cap, {bytes_per_token(G)}], got {tuple(codes.shape)}")
+    if W_kv.shape[0] != 2 * n_kv * d_h:
+        raise ValueError(f"W_kv must have {2 * n_kv * d_h} rows, got {W_kv.shape[0]}")
+    if seq_lens.shape[0] != B or tuple(out.shape) != (B, n_q, d_h):
+        raise ValueError("seq_lens / out shape mismatch")
+    return B, n_q, d_h, G, codes.shape[1]
+
+
+def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes: torch.Tensor,
+                    W_kv: torch.Tensor, seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step of one layer: codes[b, seq_lens[b] - 1] = pack(FSQ(E x_new[b]))
+    for every sequence with 1 <= seq_lens[b] <= cap, then out = attention over the
+    cache as in fsq_decode_attn. seq_lens already counts the new token.
+
+    x_new [B, C] bf16, E [G, C] bf16; the other arguments as fsq_decode_attn."""
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
+    _dev(x_new, "x_new", torch.bfloat16, 2)
+    _dev(E, "E", torch.bfloat16, 2)
+    C = x_new.shape[1]
+    if x_new.shape[0] != B or tuple(E.shape) != (G, C):
+        raise ValueError(f"x_new must be [{B}, C] and E [{G}, C], got {tuple(x_new.shape)}, "
+                         f"{tuple(E.shape)}")
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, G, cap, q.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    rc = lib().fsq_decode_step(x_new.data_ptr(), E.data_ptr(), q.data_ptr(), codes.data_ptr(),
+                               W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q, n_kv,
+                               d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc, "fsq_decode_step")
+    return out
+
+
 def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, seq_lens: torch.Tensor,
                     out: torch.Tensor, n_kv: int, workspace: torch.Tensor | None = None,
                     stream=None, split_events=None) -> torch.Tensor:
@@ -126,20 +171,7 @@ def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, se
     seq_lens [B] int32 (device), out [B, n_q, d_h] bf16. With split_events =
     (start, stop) (torch.cuda.Event with timing) the call goes through
     fsq_decode_attn_timed and the events bracket the split-K kernel."""
-    _dev(q, "q", torch.bfloat16, 3)
-    _dev(codes, "codes", torch.uint8, 3)
-    _dev(W_kv, "W_kv", torch.bfloat16, 2)
-    _dev(seq_lens, "seq_lens", torch.int32, 1)
-    _dev(out, "out", torch.bfloat16, 3)
-    B, n_q, d_h = q.shape
-    G = W_kv.shape[1]
-    cap = codes.shape[1]
-    if codes.shape[0] != B or codes.shape[2] != bytes_per_token(G):
-        raise ValueError(f"codes must be [{B}, cap, {bytes_per_token(G)}], got {tuple(codes.shape)}")
-    if W_kv.shape[0] != 2 * n_kv * d_h:
-        raise ValueError(f"W_kv must have {2 * n_kv * d_h} rows, got {W_kv.shape[0]}")
-    if seq_lens.shape[0] != B or tuple(out.shape) != (B, n_q, d_h):
-        raise ValueError("seq_lens / out shape mismatch")
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
     if workspace is None:
         workspace = alloc_workspace(B, n_q, G, cap, q.device)
     _dev(workspace, "workspace", torch.uint8, 1)

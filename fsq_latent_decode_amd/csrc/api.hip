@@ -10,7 +10,8 @@ hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, i
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                          const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
-                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, const uint16_t *x_new,
+                         const uint16_t *E, int C);
 }  // namespace fsq
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -49,7 +50,8 @@ size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t
 static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
-                         size_t workspace_bytes, void *stream, void *ev0, void *ev1) {
+                         size_t workspace_bytes, void *stream, void *ev0, void *ev1,
+                         const uint16_t *x_new = nullptr, const uint16_t *E = nullptr, int32_t C = 0) {
     if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
     if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH) return FSQ_ERR_UNSUPPORTED;
@@ -63,7 +65,7 @@ static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t
     if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
                                       seq_cap, workspace, (hipStream_t)stream, (hipEvent_t)ev0,
-                                      (hipEvent_t)ev1);
+                                      (hipEvent_t)ev1, x_new, E, C);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
 }
 
@@ -83,6 +85,20 @@ int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_
     if (!split_start || !split_stop) return FSQ_ERR_NULL;
     return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
                          workspace, workspace_bytes, stream, split_start, split_stop);
+}
+
+int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q, uint8_t *codes,
+                    const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int32_t batch,
+                    int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (C < 1) return FSQ_ERR_SHAPE;
+    if (batch >= 1 && n_q >= 1 && n_kv >= 1 && d_h >= 1 && G >= 1 && seq_cap >= 0) {
+        if (C % 8 != 0) return FSQ_ERR_UNSUPPORTED;
+        if (!x_new || !E) return FSQ_ERR_NULL;
+        if (!aligned16(x_new) || !aligned16(E)) return FSQ_ERR_UNSUPPORTED;
+    }
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
+                         workspace_bytes, stream, nullptr, nullptr, x_new, E, C);
 }
 
 }  // extern "C"

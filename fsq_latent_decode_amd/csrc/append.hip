@@ -9,73 +9,18 @@
 //   append_gemv_kernel  n < 32 (a decode step appends one token per sequence):
 //                       one CTA per output byte (a pair of coordinates) and up to
 //                       8 tokens, 16-byte vector loads of E and x, tree reduction.
+#include "append_gemv.h"
 #include "common.h"
 
 namespace fsq {
 
 constexpr int kAppendWaves = 4;
-constexpr int kGemvTokens = 8;
-
-__device__ inline float dot8_bf16(u32x4 a, u32x4 b) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
-        s += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(b[i] & 0xFFFF0000u);
-    }
-    return s;
-}
 
 template <int NT>
-__global__ __launch_bounds__(256) void append_gemv_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ E,
-                                                          uint8_t *__restrict__ codes, int n, int C,
-                                                          int G, float shift) {
-    __shared__ float red[kAppendWaves][NT][2];
-    const int j = blockIdx.x;            // output byte = coordinates 2j, 2j+1
-    const int tb = blockIdx.y * NT;      // first token of this CTA
-    const int nt = (n - tb) < NT ? (n - tb) : NT;
-    const int c0 = 2 * j, c1 = 2 * j + 1;
-    const bool has1 = c1 < G;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float acc[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = 0.0f;
-    const int nv = C / 8;
-    const u32x4 *e0p = reinterpret_cast<const u32x4 *>(E + (size_t)c0 * C);
-    const u32x4 *e1p = reinterpret_cast<const u32x4 *>(E + (size_t)(has1 ? c1 : c0) * C);
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        const u32x4 e0 = e0p[v];
-        const u32x4 e1 = has1 ? e1p[v] : u32x4{};
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-                const u32x4 xv = reinterpret_cast<const u32x4 *>(x + (size_t)(tb + t) * C)[v];
-                acc[t][0] += dot8_bf16(e0, xv);
-                acc[t][1] += dot8_bf16(e1, xv);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            float a = acc[t][c];
-            for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off);
-            if (lane == 0) red[wave][t][c] = a;
-        }
-    __syncthreads();
-    if (threadIdx.x < nt) {
-        const int t = threadIdx.x;
-        float u0 = 0.0f, u1 = 0.0f;
-        for (int w = 0; w < kAppendWaves; ++w) {
-            u0 += red[w][t][0];
-            u1 += red[w][t][1];
-        }
-        const uint32_t q0 = fsq_code(u0, shift);
-        const uint32_t q1 = has1 ? fsq_code(u1, shift) : 0u;
-        codes[(size_t)(tb + t) * bytes_per_token(G) + j] = (uint8_t)(q0 | (q1 << 4));
-    }
+__global__ __launch_bounds__(kGemvWaves * 64) void append_gemv_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ E, uint8_t *__restrict__ codes, int n,
+    int C, int G, float shift) {
+    append_gemv_body<NT>(blockIdx.x, blockIdx.y * NT, x, E, codes, n, C, G, shift, nullptr, 0);
 }
 
 template <int GP>
@@ -144,9 +89,9 @@ static hipError_t launch_append_mfma(const uint16_t *x, const uint16_t *E, uint8
 
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
                          int G, hipStream_t st) {
-    const float shift = (float)atanh((double)kDelta / (double)kH);
+    const float shift = host_fsq_shift();
     if (n < 32) {
-        const int nt = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : kGemvTokens;
+        const int nt = gemv_tokens_per_cta(n);
         dim3 grid(bytes_per_token(G), (unsigned)((n + nt - 1) / nt));
         switch (nt) {
             case 1: append_gemv_kernel<1><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;

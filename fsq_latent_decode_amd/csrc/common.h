@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace fsq {
@@ -31,6 +32,10 @@ __device__ inline uint16_t f32_to_bf16(float f) {
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
+
+// atanh(delta / h), the Eq. 2 shift, evaluated in double on the host and
+// passed to the kernels as fp32.
+inline float host_fsq_shift() { return (float)atanh((double)kDelta / (double)kH); }
 
 // Eq. 2 forward value in fp32 and the code = level + 8.
 __device__ inline uint32_t fsq_code(float u, float shift) {

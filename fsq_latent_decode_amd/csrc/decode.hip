@@ -19,6 +19,7 @@
 //                       chunks' zbar, then out = W_v,g zbar
 #include <hip/hip_ext.h>
 
+#include "append_gemv.h"
 #include "common.h"
 #include "decode_plan.h"
 
@@ -82,18 +83,15 @@ __device__ inline void bf16_vec_to_f32(const typename VecT<VW>::T &v, float *f) 
 }
 
 template <int VW>
-__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict__ q,
-                                                     const uint16_t *__restrict__ W_kv,
-                                                     _Float16 *__restrict__ qt, int G, int GP,
-                                                     int n_q, int nqp, int n_kv, int d_h,
-                                                     float scale) {
+__device__ inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
+                                   const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
+                                   int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale) {
     using A = AbsorbCfg<VW>;
     using VT = typename VecT<VW>::T;
     __shared__ float qs[kAbsorbHeads][kMaxDh];
     __shared__ float red[A::DG][kAbsorbHeads][kAbsorbCols];
-    const int g = blockIdx.x, b = blockIdx.z;
     const int tid = threadIdx.x, cg = tid % A::CG, dg = tid / A::CG;
-    const int k0 = blockIdx.y * kAbsorbCols + cg * VW;
+    const int k0 = cblk * kAbsorbCols + cg * VW;
     const bool kin = k0 < G;                  // G % VW == 0: the group is all in or all out
     const int grp = n_q / n_kv;
     // W_k rows of this thread: loads issued unconditionally from clamped addresses
@@ -143,7 +141,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
         __syncthreads();
         for (int o = tid; o < nh * kAbsorbCols; o += blockDim.x) {
             const int j = o / kAbsorbCols, col = o - j * kAbsorbCols;
-            const int k = blockIdx.y * kAbsorbCols + col;
+            const int k = cblk * kAbsorbCols + col;
             if (k < GP) {
                 float sum = 0.0f;
                 for (int r = 0; r < A::DG; ++r) sum += red[r][j][col];
@@ -153,6 +151,64 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
         }
         __syncthreads();
     }
+}
+
+template <int VW>
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict__ q,
+                                                     const uint16_t *__restrict__ W_kv,
+                                                     _Float16 *__restrict__ qt, int G, int GP,
+                                                     int n_q, int nqp, int n_kv, int d_h,
+                                                     float scale) {
+    absorb_body<VW>(blockIdx.x, blockIdx.y, blockIdx.z, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
+}
+
+// ---------------------------------------------------------- decode step
+// One launch for the two independent first stages of a decode step: CTAs
+// [0, n_app) append the new token of each sequence (output byte j = bx % P of
+// tokens (bx / P) NT ..) at row seq_lens[b] - 1 of its cache, the rest absorb
+// the queries (kv head, 64-column block, sequence). The split kernel that
+// follows sees the appended rows.
+struct StepAppend {
+    const uint16_t *x_new, *E;
+    uint8_t *codes;
+    int C;
+    float shift;
+};
+
+template <int NT, int VW>
+__global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int32_t *__restrict__ seq_lens,
+                                                        int64_t seq_cap, int batch, int n_app,
+                                                        const uint16_t *__restrict__ q,
+                                                        const uint16_t *__restrict__ W_kv,
+                                                        _Float16 *__restrict__ qt, int G, int GP,
+                                                        int n_q, int nqp, int n_kv, int d_h, float scale) {
+    const int bx = blockIdx.x;
+    if (bx < n_app) {
+        const int P = bytes_per_token(G);
+        append_gemv_body<NT>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.shift,
+                             seq_lens, seq_cap);
+    } else {
+        const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
+        int r = bx - n_app;
+        const int g = r % n_kv;
+        r /= n_kv;
+        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
+    }
+}
+
+template <int NT>
+static void launch_step_prep_nt(int vw, dim3 grid, hipStream_t st, const StepAppend &ap,
+                                const int32_t *seq_lens, int64_t seq_cap, int batch, int n_app,
+                                const uint16_t *q, const uint16_t *W_kv, _Float16 *qt, int G, int GP,
+                                int n_q, int nqp, int n_kv, int d_h, float scale) {
+#define FSQ_PREP_ARGS ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale
+    switch (vw) {
+        case 8: step_prep_kernel<NT, 8><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        case 4: step_prep_kernel<NT, 4><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        case 2: step_prep_kernel<NT, 2><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        default: step_prep_kernel<NT, 1><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS);
+    }
+#undef FSQ_PREP_ARGS
 }
 
 // ----------------------------------------------------------------- split
@@ -247,9 +303,20 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         _Float16 *qsm = reinterpret_cast<_Float16 *>(zsm);   // the tile region is free here
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
         constexpr int NQ16 = 32 * GP / 8;                    // 16-byte chunks
-        for (int i = threadIdx.x; i < NQ16; i += NW * 64) {
+        constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
+        // every load is issued before the first LDS write (clamped index, guarded store)
+        u32x4 qreg[NQI];
+#pragma unroll
+        for (int u = 0; u < NQI; ++u) {
+            const int i = threadIdx.x + u * NW * 64;
+            qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < NQI; ++u) {
+            const int i = threadIdx.x + u * NW * 64;
             const int r = i / (GP / 8), c = i - r * (GP / 8);
-            *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qsrc[i];
+            if (NQ16 % (NW * 64) == 0 || i < NQ16)
+                *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
         }
         __syncthreads();
 #pragma unroll
@@ -350,42 +417,47 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         }
 
         // ---- phase 3: pool the round's tiles for this wave's coordinate blocks.
-        // Block cb = wave + 4 j; when CB is a multiple of 4 every wave owns CBW
+        // Block cb = wave + NW j; when CB is a multiple of NW every wave owns CBW
         // blocks (known at compile time), otherwise ownership is wave-uniform.
+        // A tile past the chunk's end holds finite levels and zero probabilities
+        // (phases 1 and 2 wrote them), so all NW tiles are pooled and the LDS
+        // operand reads of tile w2 + 1 are issued before the MFMAs of tile w2.
         const int wv = __builtin_amdgcn_readfirstlane(wave);
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            if (r0 + w2 * kTile >= c1) break;     // empty tile (uniform)
+        half8 pb[2][2];
+        shortx4 za[2][2][CBW][2];
+        auto read_ops = [&](int w2, half8 (&pbo)[2], shortx4 (&zao)[2][CBW][2]) {
             const uint32_t *zt = zsm + w2 * C::kTileDw;
-            half8 pb[2];
-            shortx4 za[2][CBW][2];
-            // all LDS operand reads of this tile first, then the MFMAs; block
-            // ownership depends only on the (scalar) wave index
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                pb[ks] = *reinterpret_cast<const half8 *>(psm + ((w2 * 2 + ks) * 64 + lane) * 16);
+                pbo[ks] = *reinterpret_cast<const half8 *>(psm + ((w2 * 2 + ks) * 64 + lane) * 16);
                 const int ra = ks * 16 + hh * 4 + mrow, rb = ra + 8;
 #pragma unroll
                 for (int j = 0; j < CBW; ++j) {
                     const int cb = wv + NW * j;
                     if (CB % NW == 0 || cb < CB) {
                         const int cdw = cb * 16 + g16 * 8 + pcol * 2;
-                        za[ks][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        zao[ks][j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (lds_s4 *)(zt + ra * RS + (cdw ^ zt_swz(ra))));
-                        za[ks][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        zao[ks][j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (lds_s4 *)(zt + rb * RS + (cdw ^ zt_swz(rb))));
                     }
                 }
             }
+        };
+        read_ops(0, pb[0], za[0]);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const int cur_b = w2 & 1;
+            if (w2 + 1 < NW) read_ops(w2 + 1, pb[cur_b ^ 1], za[cur_b ^ 1]);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int j = 0; j < CBW; ++j) {
                     if (CB % NW == 0 || wv + NW * j < CB) {
-                        const short8 zs = {za[ks][j][0][0], za[ks][j][0][1], za[ks][j][0][2], za[ks][j][0][3],
-                                           za[ks][j][1][0], za[ks][j][1][1], za[ks][j][1][2], za[ks][j][1][3]};
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, zs), pb[ks],
-                                                                        acc[j], 0, 0, 0);
+                        const shortx4 lo = za[cur_b][ks][j][0], hi = za[cur_b][ks][j][1];
+                        const short8 zs = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, zs),
+                                                                        pb[cur_b][ks], acc[j], 0, 0, 0);
                     }
                 }
         }
@@ -608,7 +680,8 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                          const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
-                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, const uint16_t *x_new,
+                         const uint16_t *E, int C) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *qt = reinterpret_cast<_Float16 *>(ws + pl.off_qt);
     _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
@@ -620,7 +693,24 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
                    : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
                    : ((G & 1) == 0 && ((uintptr_t)W_kv & 3) == 0) ? 2
                                                                    : 1;
-    if (pl.S > 0) {
+    if (pl.S > 0 && x_new) {
+        // decode step: append + absorb in one launch
+        const StepAppend ap{x_new, E, const_cast<uint8_t *>(codes), C, host_fsq_shift()};
+        const int nt = gemv_tokens_per_cta(batch);
+        const int n_app = bytes_per_token(G) * ((batch + nt - 1) / nt);
+        const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
+        const dim3 grid((unsigned)(n_app + n_abs));
+#define FSQ_PREP_CALL(NT) \
+    launch_step_prep_nt<NT>(vw, grid, st, ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale)
+        switch (nt) {
+            case 1: FSQ_PREP_CALL(1); break;
+            case 2: FSQ_PREP_CALL(2); break;
+            case 4: FSQ_PREP_CALL(4); break;
+            default: FSQ_PREP_CALL(kGemvTokens);
+        }
+#undef FSQ_PREP_CALL
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (pl.S > 0) {
         dim3 ag(n_kv, (pl.GP + kAbsorbCols - 1) / kAbsorbCols, batch);
         switch (vw) {
             case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
@@ -629,6 +719,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
             default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (pl.S > 0) {
         switch (pl.GP) {
 #define FSQ_SPLIT_CASE(X)                                                                             \
     case X:                                                                                           \

@@ -142,6 +142,34 @@ int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_
                           int64_t seq_cap, void *workspace, size_t workspace_bytes,
                           void *stream, void *split_start, void *split_stop);
 
+/*
+ * fsq_decode_step - one decode step of one layer: append each sequence's new
+ * token to its cache, then attend over the cache including that token.
+ *
+ * The caller has already counted the new token in seq_lens. For every sequence
+ * b with 1 <= seq_lens[b] <= seq_cap, row seq_lens[b] - 1 of codes[b] is set to
+ * the packed codes of Q_FSQ(E x_new[b]) (Eq. 4 with the Eq. 2 forward value, as
+ * fsq_append); sequences with seq_lens[b] outside that range get no append.
+ * Then out is computed exactly as by fsq_decode_attn. The results are
+ * bit-identical to fsq_append of each new row (one token per call) followed by
+ * fsq_decode_attn with the same arguments; the difference is that the append
+ * and the query absorption share one kernel launch.
+ *   x_new    [batch, C]   bf16, 16-byte aligned: the new token of each sequence.
+ *   E        [G, C]       bf16, 16-byte aligned.
+ *   codes    [batch, seq_cap, ceil(G/2)] u8, 16-byte aligned; read, and row
+ *                          seq_lens[b] - 1 of each sequence written.
+ *   q, W_kv, seq_lens, out, workspace: as fsq_decode_attn (workspace size from
+ *                          fsq_decode_workspace_bytes(batch, n_q, G, seq_cap)).
+ * Sizes: as fsq_decode_attn, and C >= 1 with C % 8 == 0.
+ * Errors: as fsq_decode_attn; also FSQ_ERR_SHAPE (C < 1), FSQ_ERR_NULL (x_new
+ *         or E NULL), FSQ_ERR_UNSUPPORTED (C % 8 != 0, x_new or E not 16-byte
+ *         aligned).
+ */
+int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q, uint8_t *codes,
+                    const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
+                    int32_t batch, int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                    int64_t seq_cap, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

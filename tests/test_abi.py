@@ -108,6 +108,30 @@ def test_append_validation_before_any_hip_call(args, status):
     assert fsq.lib().fsq_append(x, E, c, n, C, G, None) == status
 
 
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    # (x_new, E, q, codes, W, lens, out, batch, C, n_q, n_kv, d_h, G, cap, ws, ws_bytes)
+    ((256, 256, 256, 256, 256, 256, 256, 1, 0, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 256, 1, 60, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((0, 256, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 0, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((264, 256, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 264, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    # the decode checks apply as well
+    ((256, 256, 256, 256, 256, 256, 256, 0, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 256, 1, 64, 32, 6, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 300, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 0, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 256, 256, 8, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 256, 64), fsq.FSQ_ERR_WORKSPACE),
+    ((256, 256, 256, 256, 256, 256, 256, 1, 64, 32, 8, 128, 256, 16, 0, 1 << 20), fsq.FSQ_ERR_WORKSPACE),
+])
+def test_decode_step_validation_before_any_hip_call(args, status):
+    (x, E, q, c, w, l, o, B, C, nq, nkv, dh, G, cap, ws, wsb) = args
+    rc = fsq.lib().fsq_decode_step(x, E, q, c, w, l, o, B, C, nq, nkv, dh, G, cap, ws, wsb, None)
+    assert rc == status
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(fsq, "_lib", None)
     monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")

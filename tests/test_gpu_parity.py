@@ -235,3 +235,91 @@ def test_decode_ragged_batch_full_size(fsq):
     ref = oracle_decode(q, packed, W, lens, w.n_kv, w.G)
     for b in range(w.batch):
         assert rel_l2(got[b], ref[b]) < REL_L2, b
+
+
+# ------------------------------------------------------------- decode step
+def run_step(fsq, x_bits, E_bits, q_bits, packed, W_bits, lens, n_kv, workspace=None):
+    codes = dev_u8(packed)
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_step(dev_bf16(x_bits), dev_bf16(E_bits), q, codes, dev_bf16(W_bits),
+                        torch.from_numpy(np.asarray(lens, np.int32)).cuda(), out, n_kv,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), out.float().cpu().numpy().astype(np.float64)
+
+
+def run_two_calls(fsq, x_bits, E_bits, q_bits, packed, W_bits, lens, n_kv):
+    """fsq_append of each sequence's new row (one token per call), then fsq_decode_attn."""
+    codes = dev_u8(packed)
+    cap = packed.shape[1]
+    x = dev_bf16(x_bits)
+    E = dev_bf16(E_bits)
+    for b, T in enumerate(lens):
+        if 1 <= T <= cap:
+            fsq.fsq_append(x[b:b + 1], E, codes[b, T - 1:T])
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn(q, codes, dev_bf16(W_bits), torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                        out, n_kv)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), out.float().cpu().numpy().astype(np.float64)
+
+
+def check_step(got_codes, got_out, x, E, q, packed, W, lens, n_kv, G):
+    """Appended rows vs the oracle's codes (tie rule), other rows untouched, and
+    the output vs the oracle's decode of the oracle-appended cache."""
+    cap = packed.shape[1]
+    app = [b for b, T in enumerate(lens) if 1 <= T <= cap]
+    ref_cache = packed.copy()
+    if app:
+        rows = np.stack([got_codes[b, lens[b] - 1] for b in app])
+        check_codes(rows, x[app], E, G)
+        new = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x[app]), synth.bf16_bits_to_f64(E)))
+        for i, b in enumerate(app):
+            ref_cache[b, lens[b] - 1] = new[i]
+    mask = np.ones(packed.shape[:2], bool)
+    for b in app:
+        mask[b, lens[b] - 1] = False
+    assert np.array_equal(got_codes[mask], packed[mask]), "a row other than the new token's changed"
+    eff = np.minimum(np.maximum(lens, 0), cap)
+    ref = oracle_decode(q, ref_cache, W, eff, n_kv, G)
+    for b in range(len(lens)):
+        if eff[b] == 0:
+            assert np.all(got_out[b] == 0)
+        else:
+            assert rel_l2(got_out[b], ref[b]) < REL_L2, b
+
+
+@pytest.mark.parametrize("B,C,n_q,n_kv,d_h,G,cap,lens", [
+    (1, 1024, 16, 8, 128, 64, 1024, [1024]),
+    (2, 512, 32, 8, 128, 84, 700, [700, 1]),                        # 2 tokens per append CTA
+    (3, 256, 12, 4, 96, 37, 300, [0, 300, 299]),                    # 4 per CTA, odd G, empty sequence
+    (5, 4096, 32, 8, 128, 256, 400, [400, 17, 1, 0, 250]),          # 8 per CTA
+    (9, 64, 8, 2, 64, 96, 100, [100, 5, 0, 1, 64, 33, 99, 100, 2]),  # two CTAs of 8 tokens per byte
+    (2, 64, 8, 1, 64, 30, 50, [60, 50]),                            # length > cap: no append, clamped
+])
+def test_decode_step_parity(fsq, B, C, n_q, n_kv, d_h, G, cap, lens):
+    q, packed, W, lens = decode_case(G * 11 + cap + B, B, n_q, n_kv, d_h, G, cap, lens)
+    g = synth.rng(210, B, G + cap)
+    x = synth.normal_bf16(g, (B, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    got_codes, got_out = run_step(fsq, x, E, q, packed, W, lens, n_kv)
+    check_step(got_codes, got_out, x, E, q, packed, W, lens, n_kv, G)
+    two_codes, two_out = run_two_calls(fsq, x, E, q, packed, W, lens, n_kv)
+    assert np.array_equal(got_codes, two_codes)
+    assert np.array_equal(got_out, two_out)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_g256", "qwen3_8b_g84"])
+def test_decode_step_full_size_layer(fsq, name):
+    """One decode step of layer 0 of the Qwen3-8B-shaped workloads at full context,
+    as the benchmark runs it: the new token is appended at row T - 1."""
+    w = synth.WORKLOADS[name]
+    E, W = synth.layer_weights(w, 0)
+    q = synth.layer_query(w, 0)
+    x = synth.layer_x(w, 0, w.batch, synth.T_XNEW)
+    lens = synth.seq_lens(w)
+    packed = synth.layer_codes(w, 0)
+    got_codes, got_out = run_step(fsq, x, E, q, packed, W, lens, w.n_kv)
+    check_step(got_codes, got_out, x, E, q, packed, W, lens, w.n_kv, w.G)
