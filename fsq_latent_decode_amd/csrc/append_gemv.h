@@ -40,15 +40,31 @@ __device__ inline void append_gemv_body(int j, int tb, const uint16_t *__restric
     const int nv = C / 8;
     const u32x4 *e0p = reinterpret_cast<const u32x4 *>(E + (size_t)c0 * C);
     const u32x4 *e1p = reinterpret_cast<const u32x4 *>(E + (size_t)(has1 ? c1 : c0) * C);
-    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-        const u32x4 e0 = e0p[v];
-        const u32x4 e1 = has1 ? e1p[v] : u32x4{};
+    // two vectors per thread and pass, all loads issued before the first use
+    // (clamped indices); each thread accumulates its vectors in index order
+    constexpr int U = 2;
+    const int nthr = kGemvWaves * 64;
+    for (int v0 = threadIdx.x; v0 < nv; v0 += U * nthr) {
+        u32x4 e0[U], e1[U], xv[U][NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-                const u32x4 xv = reinterpret_cast<const u32x4 *>(x + (size_t)(tb + t) * C)[v];
-                acc[t][0] += dot8_bf16(e0, xv);
-                acc[t][1] += dot8_bf16(e1, xv);
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * nthr < nv ? v0 + u * nthr : nv - 1;
+            e0[u] = e0p[v];
+            e1[u] = has1 ? e1p[v] : u32x4{};
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t < nt) xv[u][t] = reinterpret_cast<const u32x4 *>(x + (size_t)(tb + t) * C)[v];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (v0 + u * nthr < nv) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t < nt) {
+                        acc[t][0] += dot8_bf16(e0[u], xv[u][t]);
+                        acc[t][1] += dot8_bf16(e1[u], xv[u][t]);
+                    }
+                }
             }
         }
     }

@@ -26,7 +26,6 @@
 namespace fsq {
 
 constexpr int kTile = 32;        // tokens per wave and round (the score MFMA's M)
-constexpr int kWaves = 4;        // waves per CTA of the absorb and merge kernels
 
 // fp16 levels of one packed dword (8 codes, nibble i = coordinate 8D + i), in
 // the operand order (c0,c4)(c1,c5)(c2,c6)(c3,c7): 0x6400 | n is the fp16 value
@@ -94,6 +93,20 @@ __device__ inline void absorb_body(int g, int cblk, int b, const uint16_t *__res
     const int k0 = cblk * kAbsorbCols + cg * VW;
     const bool kin = k0 < G;                  // G % VW == 0: the group is all in or all out
     const int grp = n_q / n_kv;
+    // q rows of heads hb .. hb + 3 of this kv head, kAbsorbHeads * kMaxDh values
+    // over the 256 threads, from clamped addresses (masked when staged)
+    static_assert(kAbsorbHeads * kMaxDh == 4 * 256, "4 q values per thread");
+    uint16_t qr[4];
+    auto load_q = [&](int hb) {
+        const int nh = (grp - hb) < kAbsorbHeads ? (grp - hb) : kAbsorbHeads;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, j = i / kMaxDh, d = i - j * kMaxDh;
+            const int jj = j < nh ? j : nh - 1, dd = d < d_h ? d : d_h - 1;
+            qr[u] = q[((size_t)b * n_q + (size_t)g * grp + hb + jj) * d_h + dd];
+        }
+    };
+    load_q(0);
     // W_k rows of this thread: loads issued unconditionally from clamped addresses
     const uint16_t *wk = W_kv + (size_t)g * d_h * G + (kin ? k0 : 0);
     VT wr[A::RMAX];
@@ -117,11 +130,11 @@ __device__ inline void absorb_body(int g, int cblk, int b, const uint16_t *__res
     }
     for (int hb = 0; hb < grp; hb += kAbsorbHeads) {
         const int nh = (grp - hb) < kAbsorbHeads ? (grp - hb) : kAbsorbHeads;
-        for (int i = tid; i < kAbsorbHeads * kMaxDh; i += blockDim.x) {
-            const int j = i / kMaxDh, d = i - j * kMaxDh;
-            qs[j][d] = (j < nh && d < d_h)
-                           ? bf16_to_f32(q[((size_t)b * n_q + (size_t)g * grp + hb + j) * d_h + d])
-                           : 0.0f;
+        if (hb > 0) load_q(hb);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, j = i / kMaxDh, d = i - j * kMaxDh;
+            qs[j][d] = (j < nh && d < d_h) ? bf16_to_f32(qr[u]) : 0.0f;
         }
         __syncthreads();
         for (int j = 0; j < nh; ++j) {
@@ -255,11 +268,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const int P = (G + 1) / 2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
-    int64_t T = seq_lens[b];
-    T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
-    const int64_t c0 = (int64_t)s * chunk;
-    if (c0 >= T) return;
-    const int64_t c1 = (c0 + chunk < T) ? c0 + chunk : T;
+    const int64_t c0 = (int64_t)s * chunk;   // < seq_cap: the grid has ceil(seq_cap / chunk) chunks
+    // The first round's loads are issued before the sequence length is known,
+    // bounded by the cache capacity (rows up to seq_cap - 1 are inside the
+    // buffer); rows past the length are masked once it has arrived.
+    int64_t c1 = (c0 + chunk < seq_cap) ? c0 + chunk : seq_cap;
     const int t = lane & 31, hh = lane >> 5;
     const uint8_t *seq = codes + (size_t)b * seq_cap * P;
 
@@ -319,6 +332,14 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
                 *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
         }
         __syncthreads();
+        // the sequence length: leave if this chunk is past it (uniform), else
+        // bound the chunk and recount the first round's tokens
+        int64_t T = seq_lens[b];
+        T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
+        if (c0 >= T) return;
+        c1 = (c0 + chunk < T) ? c0 + chunk : T;
+        const int64_t rem0 = c1 - (c0 + wave * kTile);
+        ld_ntok = rem0 <= 0 ? 0 : (rem0 < kTile ? (int)rem0 : kTile);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             qv[kb] = *reinterpret_cast<const half8 *>(qsm + t * QROW + 16 * kb + 8 * hh);
@@ -507,7 +528,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
     int chunk, int S) {
     using VT = typename VecT<VW>::T;
-    constexpr int NVT = kMaxG / VW / 2;   // W_v vectors per thread (two or more threads per row)
+    // W_v vectors per thread held in registers (two or more threads per row);
+    // narrow vectors (odd G) beyond 32 per thread are read in the dot loop
+    constexpr int NVT = (kMaxG / VW / 2) < 32 ? (kMaxG / VW / 2) : 32;
     __shared__ float coef[kMergeMl * 256];
     __shared__ float zpart[256 * 8];   // [split group][GP]
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
@@ -515,22 +538,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
-    int64_t T = seq_lens[b];
-    T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
-    const int ns = (int)((T + chunk - 1) / chunk);
-    if (ns == 0) {
-        for (int d = tid; d < d_h; d += blockDim.x) o[d] = 0;
-        return;
-    }
     const size_t srow = (size_t)n_q;   // rows between splits
 
+    // The loads below are issued over all S splits of the workspace (indices
+    // clamped to S - 1) before the sequence length arrives; entries of splits
+    // at or past the sequence's split count ns are discarded by selects.
     // ---- issue: (m, l) pairs
     const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (size_t)b * S * n_q + h;
     float2 mlr[kMergeMl];
 #pragma unroll
     for (int u = 0; u < kMergeMl; ++u) {
         const int i = tid + 256 * u;
-        mlr[u] = ml[(size_t)(i < ns ? i : ns - 1) * srow];
+        mlr[u] = ml[(size_t)(i < S ? i : S - 1) * srow];
     }
     // ---- issue: first batch of partial rows (thread = 8-position group kg, split group sg)
     const int KG = GP / 8, SG = 256 / KG;
@@ -541,7 +560,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll
     for (int u = 0; u < kMergeRows; ++u) {
         const int i = sg + u * SG;
-        v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(zthr && i < ns ? i : 0) * srow * GP);
+        v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(zthr && i < S ? i : 0) * srow * GP);
     }
     // ---- issue: W_v row d, vectors part, part + TPR, ... (TPR >= 2 threads per row)
     const int g = h / (n_q / n_kv);
@@ -562,7 +581,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
         }
     }
 
-    // ---- M and L over all splits (the (m, l) loads are the oldest in flight)
+    int64_t T = seq_lens[b];
+    T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
+    const int ns = (int)((T + chunk - 1) / chunk);
+
+    // ---- M and L over the sequence's splits (the (m, l) loads are the oldest in flight)
     float M = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kMergeMl; ++u)
@@ -570,6 +593,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     if (lane == 0) red[wave] = M;
     __syncthreads();
+    if (ns == 0) {   // empty sequence (uniform): the output is zero
+        for (int d = tid; d < d_h; d += blockDim.x) o[d] = 0;
+        return;
+    }
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float Lp = 0.0f;
 #pragma unroll
@@ -592,9 +619,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll
         for (int u = 0; u < kMergeRows; ++u) {
             const int i = sg + u * SG;
-            const float c = i < ns ? coef[i] : 0.0f;
+            const bool ok = i < ns;
+            const float c = coef[ok ? i : 0];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] += c * (float)v[u][j];
+            for (int j = 0; j < 8; ++j) a[j] += ok ? c * (float)v[u][j] : 0.0f;
         }
         for (int i0 = sg + kMergeRows * SG; i0 < ns; i0 += kMergeRows * SG) {   // long caches
 #pragma unroll
@@ -633,6 +661,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll
                 for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
             }
+        }
+        for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
+            float wf[VW];
+            bf16_vec_to_f32<VW>(wrow[vi], wf);
+#pragma unroll
+            for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
         }
         for (int off = TPR >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
         if (part == 0 && drow) o[d] = f32_to_bf16(acc);

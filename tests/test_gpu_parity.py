@@ -151,6 +151,8 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     (1, 32, 8, 128, 160, 5000, [4999]),
     (1, 8, 2, 256, 64, 100, [100]),              # d_h 256: one thread per output row
     (2, 16, 4, 64, 30, 300, [300, 7]),           # G % 4 == 2: 4-byte W_v loads
+    (1, 8, 2, 128, 131, 64, [64]),               # odd G: W_v vectors past the register set
+    (1, 4, 1, 128, 130, 90, [90]),               # G % 4 == 2: the same with 2-wide vectors
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
