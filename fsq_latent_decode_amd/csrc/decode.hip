@@ -11,10 +11,13 @@
 //
 // Three launches per call, all on the caller's stream:
 //   absorb_kernel       q~ = (log2 e / sqrt d_h) W_k,g^T q -> fp16, operand order
+//                       (step_prep_kernel in a decode step: the same absorption
+//                       plus the append of each sequence's new token)
 //   decode_split_kernel one CTA per (token chunk, sequence, 32-head group):
-//                       codes -> registers (prefetched one tile ahead) -> LDS ->
-//                       fp16 levels -> MFMA scores (all heads share z) -> online
-//                       softmax (exp2) -> MFMA latent pooling -> (m, l, zbar fp16)
+//                       codes -> registers (prefetched one round ahead) -> fp16
+//                       operands -> MFMA scores (all heads share z) -> LDS tile
+//                       -> online softmax (exp2) -> MFMA latent pooling ->
+//                       (m, l, zbar fp16)
 //   decode_merge_kernel one CTA per (sequence, head): log-sum-exp merge of the
 //                       chunks' zbar, then out = W_v,g zbar
 #include <hip/hip_ext.h>
@@ -27,23 +30,20 @@ namespace fsq {
 
 constexpr int kTile = 32;        // tokens per wave and round (the score MFMA's M)
 
-// fp16 levels of one packed dword (8 codes, nibble i = coordinate 8D + i), in
-// the operand order (c0,c4)(c1,c5)(c2,c6)(c3,c7): 0x6400 | n is the fp16 value
-// 1024 + n, so subtracting 1032 gives the level n - 8 exactly.
-__device__ inline half8 unpack_levels(uint32_t w) {
-    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-    const uint32_t m = 0x000F000Fu, e = 0x64006400u;
-    const uint32_t t0 = (w & m) | e;
-    const uint32_t t1 = ((w >> 4) & m) | e;
-    const uint32_t t2 = ((w >> 8) & m) | e;
-    const uint32_t t3 = ((w >> 12) & m) | e;
-    const half2v bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const half2v h0 = __builtin_bit_cast(half2v, t0) - bias;
-    const half2v h1 = __builtin_bit_cast(half2v, t1) - bias;
-    const half2v h2 = __builtin_bit_cast(half2v, t2) - bias;
-    const half2v h3 = __builtin_bit_cast(half2v, t3) - bias;
-    const half8 r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-    return r;
+// Codes of one packed dword (8 codes, nibble i = coordinate 8D + i) as fp16
+// operands in the order (c0,c4)(c1,c5)(c2,c6)(c3,c7). The bit pattern n of a
+// code is the fp16 subnormal n * 2^-24, exact, so no bias is subtracted here:
+// with z = n - 8 and n' = n * 2^-24,
+//   q~ . z = 2^24 (q~ . n') - 8 sum_k q~_k,
+// where the last term is the same for every token of a head and cancels in the
+// softmax (and in the merge of splits, which share it), and
+//   sum_t p_t z_t / sum_t p_t = 2^24 sum_t p_t n'_t / sum_t p_t - 8
+// when the denominator sums the same fp16 p_t that the pooling MFMA uses.
+constexpr float kCodeScale = 16777216.0f;   // 2^24
+__device__ inline half8 unpack_codes(uint32_t w) {
+    const uint32_t m = 0x000F000Fu;
+    const u32x4 t = {w & m, (w >> 4) & m, (w >> 8) & m, (w >> 12) & m};
+    return __builtin_bit_cast(half8, t);
 }
 
 // ---------------------------------------------------------------- absorb
@@ -166,13 +166,18 @@ __device__ inline void absorb_body(int g, int cblk, int b, const uint16_t *__res
     }
 }
 
+// Absorption launch of fsq_decode_attn: one CTA per (kv head, 64-column
+// block, sequence), in a 1-D grid.
 template <int VW>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict__ q,
                                                      const uint16_t *__restrict__ W_kv,
                                                      _Float16 *__restrict__ qt, int G, int GP,
-                                                     int n_q, int nqp, int n_kv, int d_h,
-                                                     float scale) {
-    absorb_body<VW>(blockIdx.x, blockIdx.y, blockIdx.z, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
+                                                     int n_q, int nqp, int n_kv, int d_h, float scale) {
+    const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
+    int r = blockIdx.x;
+    const int g = r % n_kv;
+    r /= n_kv;
+    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
 }
 
 // ---------------------------------------------------------- decode step
@@ -196,8 +201,8 @@ __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int
                                                         _Float16 *__restrict__ qt, int G, int GP,
                                                         int n_q, int nqp, int n_kv, int d_h, float scale) {
     const int bx = blockIdx.x;
+    const int P = bytes_per_token(G);
     if (bx < n_app) {
-        const int P = bytes_per_token(G);
         append_gemv_body<NT>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.shift,
                              seq_lens, seq_cap);
     } else {
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     typedef short short8 __attribute__((ext_vector_type(8)));
 
     for (int64_t r0 = c0; r0 < c1; r0 += NW * kTile) {
-        // ---- phase 1: own tile -> levels -> fp16 tile + scores
+        // ---- phase 1: own tile -> fp16 codes -> LDS tile + scores
         uint32_t cur[KB];
         const int ntok = ld_ntok;
         const int sh = ld_sh;
@@ -372,24 +377,19 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         }
         issue(r0 + NW * kTile + wave * kTile);
 
-        const bool live = t < ntok;
-        floatx16 sc0 = floatx16{}, sc1 = floatx16{};
+        // No masking of the loaded words: tokens past the chunk's end (rows
+        // clamped into the cache) get probability 0 below, and coordinates in
+        // the padding G..GP-1 (bytes of the next row) meet zero q~ entries and
+        // are never read back from the pooled sums; all codes are finite.
+        // Scores are accumulated in units of 2^-24 (unpack_codes) and scaled
+        // when they enter the max and the exponent.
+        floatx16 sc = floatx16{};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            uint32_t w = cur[kb];
-            if (!AL) {
-                const int nvalid = P - hh * (GP / 4) - 4 * kb;
-                w &= nvalid <= 0 ? 0u : nvalid >= 4 ? 0xFFFFFFFFu : (1u << (8 * nvalid)) - 1u;
-            }
-            w = live ? w : 0u;
-            const half8 z = unpack_levels(w);
+            const half8 z = unpack_codes(cur[kb]);
             *reinterpret_cast<half8 *>(zt_own + t * RS + ((8 * kb + 4 * hh) ^ zt_swz(t))) = z;
-            if (kb & 1)
-                sc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc1, 0, 0, 0);
-            else
-                sc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc0, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc, 0, 0, 0);
         }
-        const floatx16 sc = sc0 + sc1;
         float sv[16];
         float tmax = -INFINITY;
 #pragma unroll
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             sv[r] = tok < ntok ? sc[r] : -INFINITY;
             tmax = fmaxf(tmax, sv[r]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kCodeScale;
         if (lane < 32) tmax_s[wave][t] = tmax;
         __syncthreads();
 
@@ -415,9 +415,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         _Float16 p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(sv[r] - m_new);
-            psum += e;
-            p[r] = (_Float16)e;
+            p[r] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[r], kCodeScale, -m_new));
+            psum += (float)p[r];   // the normaliser sums the fp16 weights the pooling uses
         }
         psum += __shfl_xor(psum, 32);
         if (lane < 32) tsum_s[wave][t] = psum;
@@ -440,7 +439,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         // ---- phase 3: pool the round's tiles for this wave's coordinate blocks.
         // Block cb = wave + NW j; when CB is a multiple of NW every wave owns CBW
         // blocks (known at compile time), otherwise ownership is wave-uniform.
-        // A tile past the chunk's end holds finite levels and zero probabilities
+        // A tile past the chunk's end holds finite codes and zero probabilities
         // (phases 1 and 2 wrote them), so all NW tiles are pooled and the LDS
         // operand reads of tile w2 + 1 are issued before the MFMAs of tile w2.
         const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -487,7 +486,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 
     // ---- epilogue: zbar = acc / l in operand-position order, fp16, stored from
     // registers: each lane holds head t and, per block, 4 runs of 4 positions
-    const float invL = 1.0f / l_run;
+    const float zscale = kCodeScale / l_run;   // codes n * 2^-24 pooled: zbar = 2^24 acc / l - 8
     const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
     const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -500,8 +499,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             if (CB % NW == 0 || cb < CB) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const half4 v = {(_Float16)(acc[j][4 * r4 + 0] * invL), (_Float16)(acc[j][4 * r4 + 1] * invL),
-                                     (_Float16)(acc[j][4 * r4 + 2] * invL), (_Float16)(acc[j][4 * r4 + 3] * invL)};
+                    const half4 v = {(_Float16)fmaf(acc[j][4 * r4 + 0], zscale, -8.0f),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 1], zscale, -8.0f),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 2], zscale, -8.0f),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 3], zscale, -8.0f)};
                     *reinterpret_cast<half4 *>(dst + cb * 32 + r4 * 8 + hh * 4) = v;
                 }
             }
@@ -745,7 +746,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
 #undef FSQ_PREP_CALL
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (pl.S > 0) {
-        dim3 ag(n_kv, (pl.GP + kAbsorbCols - 1) / kAbsorbCols, batch);
+        const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
+        const dim3 ag((unsigned)n_abs);
         switch (vw) {
             case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
             case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
