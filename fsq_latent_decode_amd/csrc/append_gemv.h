@@ -25,7 +25,7 @@ __device__ inline float dot8_bf16(u32x4 a, u32x4 b) {
 // otherwise row lens[i] - 1 of sequence i in a [n, seq_cap, P] cache, skipped
 // unless 1 <= lens[i] <= seq_cap. The per-token arithmetic does not depend on NT.
 template <int NT>
-__device__ inline void append_gemv_body(int j, int tb, const uint16_t *__restrict__ x,
+__device__ __attribute__((always_inline)) inline void append_gemv_body(int j, int tb, const uint16_t *__restrict__ x,
                                         const uint16_t *__restrict__ E, uint8_t *__restrict__ codes,
                                         int n, int C, int G, float shift,
                                         const int32_t *__restrict__ lens, int64_t seq_cap) {

@@ -82,7 +82,7 @@ __device__ inline void bf16_vec_to_f32(const typename VecT<VW>::T &v, float *f) 
 }
 
 template <int VW>
-__device__ inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
+__device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
                                    int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale) {
     using A = AbsorbCfg<VW>;

@@ -34,11 +34,11 @@ def rng(workload_id: int, layer: int, tensor_id: int) -> np.random.Generator:
 # ---------------------------------------------------------------- bf16 formats
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even) and
-    return the 16-bit patterns as uint16. Inputs here are finite normals."""
+    return the 16-bit patterns as uint16. Inputs here are finite; their bit
+    patterns are at most 0xFF7FFFFF, so the 32-bit sum below cannot wrap."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + lsb) >> 16
+    u = a.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -138,6 +138,14 @@ def layer_query(w: Workload, layer: int) -> np.ndarray:
 
 def layer_x(w: Workload, layer: int, n_tokens: int, tensor_id: int = T_X) -> np.ndarray:
     return normal_bf16(rng(w.wid, layer, tensor_id), (n_tokens, w.C), 1.0)
+
+
+def layer_x_chunk(w: Workload, layer: int, chunk: int, chunk_tokens: int = 8192) -> np.ndarray:
+    """Residual states of prefill chunk `chunk` (tokens chunk * chunk_tokens ..), for
+    caches built by appending chunk after chunk (the million-token workload);
+    each chunk has its own seed [workload, layer, T_X, chunk]."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.wid, layer, T_X, chunk])))
+    return normal_bf16(g, (chunk_tokens, w.C), 1.0)
 
 
 def layer_codes(w: Workload, layer: int, lens: np.ndarray | None = None, cap: int | None = None) -> np.ndarray:

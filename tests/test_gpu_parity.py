@@ -325,3 +325,53 @@ def test_decode_step_full_size_layer(fsq, name):
     packed = synth.layer_codes(w, 0)
     got_codes, got_out = run_step(fsq, x, E, q, packed, W, lens, w.n_kv)
     check_step(got_codes, got_out, x, E, q, packed, W, lens, w.n_kv, w.G)
+
+
+def test_million_token_workload_layer0(fsq):
+    """The million-token G=84 workload, layer 0, full size. Its cache holds
+    codes = FSQ(E x) of 128 prefill chunks of 8192 tokens (x ~ N(0,1) bf16 per
+    chunk). The oracle encodes every chunk into a reference cache; the GPU
+    appends the same chunks (codes compared under the tie rule, one chunk at a
+    time) and decodes over the reference cache (compared with the oracle's
+    decode of it)."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = synth.WORKLOADS["qwen3_8b_g84_1m"]
+    chunk = 8192
+    n_chunks = w.context // chunk
+    E, W = synth.layer_weights(w, 0)
+    Ef = synth.bf16_bits_to_f64(E)
+    E_dev = dev_bf16(E)
+    ref_cache = np.empty((w.context, w.P), np.uint8)
+    gpu_cache = torch.zeros((w.context, w.P), dtype=torch.uint8, device="cuda")
+    flips = 0
+    depth = 6
+    with ThreadPoolExecutor(depth) as ex:
+        futs = [ex.submit(synth.layer_x_chunk, w, 0, c, chunk) for c in range(min(depth, n_chunks))]
+        for c in range(n_chunks):
+            x = futs[c].result()
+            if c + depth < n_chunks:
+                futs.append(ex.submit(synth.layer_x_chunk, w, 0, c + depth, chunk))
+            rows = slice(c * chunk, (c + 1) * chunk)
+            fsq.fsq_append(dev_bf16(x), E_dev, gpu_cache[rows])
+            u = orc.projection(synth.bf16_bits_to_f64(x), Ef)
+            ref = orc.fsq_codes(u)
+            ref_cache[rows] = orc.pack_codes(ref)
+            got = orc.unpack_codes(gpu_cache[rows].cpu().numpy(), w.G)
+            diff = got.astype(int) - ref.astype(int)
+            bad = np.nonzero(diff)
+            if len(bad[0]):
+                assert np.all(np.abs(diff) <= 1), f"chunk {c}: a code differs by more than 1"
+                ut = orc.fsq_bound(u[bad])
+                dist = np.abs(ut - (np.floor(ut) + 0.5))
+                assert np.all(dist < TIE_TOL), f"chunk {c}: flip away from a tie ({dist.max()})"
+            flips += len(bad[0])
+    assert flips <= FLIP_RATE * w.context * w.G, f"{flips} flipped codes"
+    # level statistics of FSQ(E x) (not uniform): every code value occurs
+    assert len(np.unique(orc.unpack_codes(ref_cache[:chunk], w.G))) == 16
+    q = synth.layer_query(w, 0)
+    lens = synth.seq_lens(w)
+    got = run_decode(fsq, q, ref_cache[None], W, lens, w.n_kv)
+    want = oracle_decode(q, ref_cache[None], W, lens, w.n_kv, w.G)
+    e = rel_l2(got, want)
+    print(f"million-token layer 0: {flips} of {w.context * w.G} codes at fp32 ties, rel L2 {e:.2e}")
+    assert e < REL_L2
