@@ -13,8 +13,10 @@ Infinity Cache from its previous use.
 
 Prints one JSON line: context-tokens/s (sum of sequence lengths / step time),
 the step's roofline fraction, the split-K kernel's roofline (HIP events from
-hipExtLaunchKernelGGL around each launch, in a second phase of eager steps), and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+hipExtLaunchKernelGGL around each launch, in a second phase of eager steps), the
+prefill append of the G=84 workload (8192 tokens through E and FSQ) with its
+roofline, and the fp64 CPU oracle timed on a bounded sample of the same workload
+(all threads and one thread), whose outputs are also compared with the GPU's.
 """
 from __future__ import annotations
 
@@ -50,6 +52,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=5,
                     help="eager steps whose split-K launches are bracketed by HIP events")
+    ap.add_argument("--no-append", action="store_true", help="skip the prefill-append measurement")
     ap.add_argument("--two-call", action="store_true",
                     help="per layer fsq_append + fsq_decode_attn instead of fsq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -179,6 +182,50 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
     return m, ms, call_ms, replicas
 
 
+def append_prefill(w, torch, calls=40):
+    """fsq_append of the workload's prefill chunk (x [n, C] -> codes [n, P]), replayed
+    from a HIP graph over replicas of x that together exceed the Infinity Cache;
+    returns the average time per call and its HBM roofline."""
+    import fsq_latent_decode_amd as fsq
+    n = w.append_tokens
+    E, _ = synth.layer_weights(w, 0)
+    x_bits = synth.layer_x(w, 0, n)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    x0 = to_dev(x_bits)
+    reps = max(2, math.ceil(4 * MALL_BYTES / x0.numel() / 2))
+    xs = [x0] + [x0.clone() for _ in range(reps - 1)]
+    Ed = to_dev(E)
+    codes = [torch.empty((n, w.P), dtype=torch.uint8, device="cuda") for _ in range(reps)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for r in range(reps):
+            fsq.fsq_append(xs[r], Ed, codes[r])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fsq.fsq_append(xs[i % reps], Ed, codes[i % reps])
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / calls
+    nbytes = n * w.C * 2 + w.G * w.C * 2 + n * w.P
+    flops = 2.0 * n * w.G * w.C
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"workload": w.name, "tokens": n, "C": w.C, "G": w.G, "us_per_call": us,
+            "tokens_per_s": n / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "bytes_per_call": nbytes,
+                         "mfma_frac": flops / (us * 1e-6) / (MFMA_FP16_PEAK_TFLOPS * 1e12)},
+            "timing": f"{calls} calls in one HIP graph over {reps} replicas of x, events around the replay"}
+
+
 def copy_probe(torch, mib):
     n = mib * 2 ** 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -191,40 +238,65 @@ def copy_probe(torch, mib):
 
 
 # --------------------------------------------------------------- CPU side
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, gpu_out=None):
     """The fp64 oracle (oracle/) as it stands, on a bounded sample of the step:
     whole layers (one-token append + decode at full context), extrapolated to
-    the workload's layer count."""
+    the workload's layer count; timed with the BLAS threads available and with
+    one thread. With gpu_out (layer -> the GPU's output of that layer in the
+    timed steps) the oracle's outputs of the sampled layers are compared with it."""
     from oracle import fsq_oracle as orc
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
     lens = synth.seq_lens(w)
-    done, t_total = 0, 0.0
-    l = 0
-    while t_total < seconds and done < w.layers:
+
+    def inputs(l):
         E, W = synth.layer_weights(w, l)
-        x = synth.bf16_bits_to_f64(synth.layer_x(w, l, w.batch, synth.T_XNEW))
-        q = synth.bf16_bits_to_f64(synth.layer_query(w, l))
-        packed = synth.layer_codes(w, l, lens=lens if w.ragged else None)
-        Wf = synth.bf16_bits_to_f64(W)
-        Ef = synth.bf16_bits_to_f64(E)
-        t = time.perf_counter()
+        return (synth.bf16_bits_to_f64(synth.layer_x(w, l, w.batch, synth.T_XNEW)),
+                synth.bf16_bits_to_f64(synth.layer_query(w, l)),
+                synth.layer_codes(w, l, lens=lens if w.ragged else None),
+                synth.bf16_bits_to_f64(W), synth.bf16_bits_to_f64(E))
+
+    def layer(x, q, packed, Wf, Ef):
         new = orc.pack_codes(orc.encode(x, Ef))
         for b in range(w.batch):
             packed[b, int(lens[b]) - 1] = new[b]
-        orc.decode_attn(q, packed, Wf, lens, w.n_kv, w.G)
-        t_total += time.perf_counter() - t
-        done += 1
-        l += 1
+        return orc.decode_attn(q, packed, Wf, lens, w.n_kv, w.G)
+
+    def run(budget, keep):
+        done, t_total, outs = 0, 0.0, {}
+        while t_total < budget and done < w.layers:
+            args = inputs(done)
+            t = time.perf_counter()
+            out = layer(*args)
+            t_total += time.perf_counter() - t
+            if keep:
+                outs[done] = out
+            done += 1
+        return done, t_total, outs
+
+    done, t_total, outs = run(seconds, True)
     per_step = t_total / done * w.layers
-    return {"value": float(np.sum(lens)) / per_step, "unit": "context-tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of {w.layers} layers (one-token append + decode at full context), "
-                      f"{t_total:.1f} s, extrapolated x{w.layers / done:.1f} to one step",
-            "step_s": per_step}
+    res = {"value": float(np.sum(lens)) / per_step, "unit": "context-tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{done} of {w.layers} layers (one-token append + decode at full context), "
+                     f"{t_total:.1f} s, extrapolated x{w.layers / done:.1f} to one step",
+           "step_s": per_step, "cpu_count": os.cpu_count(),
+           "affinity_cores": len(os.sched_getaffinity(0))}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, t1, _ = run(seconds / 2, False)
+        res["one_thread"] = {"value": float(np.sum(lens)) / (t1 / d1 * w.layers), "layers": d1,
+                             "seconds": t1}
+    if gpu_out:
+        errs = [float(np.linalg.norm(gpu_out[l] - outs[l]) / np.linalg.norm(outs[l]))
+                for l in sorted(outs) if l in gpu_out]
+        res["parity"] = {"layers": len(errs), "max_rel_l2": max(errs) if errs else None,
+                         "bar": 5e-3, "what": "GPU output of the timed steps vs the oracle, same layers"}
+    return res
 
 
 def split_kernel_bytes(w, lens):
@@ -291,6 +363,7 @@ def main():
     m, ms, call_ms, reps = run_workload(w, torch, args.steps, args.warmup, args.eager,
                                         args.timing_steps, args.two_call)
     main_res = summarize(w, ms, call_ms, reps)
+    gpu_out = {l: d["out"].float().cpu().numpy().astype(np.float64) for l, d in enumerate(m.reps[0])}
     del m
     torch.cuda.empty_cache()
     also = {}
@@ -301,7 +374,12 @@ def main():
         also[name] = summarize(w2, ms2, cm2, reps2)
         del m2
         torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    app = None
+    for name in [args.workload] + [s for s in args.also.split(",") if s]:
+        if synth.WORKLOADS[name].append_tokens and not args.no_append:
+            app = append_prefill(synth.WORKLOADS[name], torch)
+            break
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, gpu_out)
     line = {
         "metric": "decode context-tokens/s",
         "value": main_res["value"],
@@ -325,6 +403,7 @@ def main():
         "roofline": main_res.get("roofline"),
         "cpu_baseline": cpu,
         "also": also,
+        "append_prefill": app,
     }
     print(json.dumps(line))
 

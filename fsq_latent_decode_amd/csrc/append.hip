@@ -23,36 +23,132 @@ __global__ __launch_bounds__(kGemvWaves * 64) void append_gemv_kernel(
     append_gemv_body<NT>(blockIdx.x, blockIdx.y * NT, x, E, codes, n, C, G, shift, nullptr, 0);
 }
 
+// Prefill path. A CTA of 4 waves computes u = E x for 32 tokens; the waves
+// split C into batches of KPB (wave w takes batches w, w + 4, ...). Each wave
+// stages its batches through a private ring of NB LDS slots holding the x tile
+// [32 rows x KPB] and the E tile [GP rows x KPB]: every load instruction moves
+// one 16-byte chunk per lane straight into LDS (global_load_lds_dwordx4, LDS
+// address = slot base + 16 * lane), so that the lanes of an instruction read
+// whole row segments (8 or 4 lanes per row) and the loads coalesce. A chunk c
+// of row r sits at slot position c ^ swz(r); the MFMA operands are then read
+// back with ds_read_b128 in their register layout (lane = row, k-step i = chunks
+// 2i and 2i + 1), 16 consecutive rows on distinct banks.
 template <int GP>
-__global__ __launch_bounds__(kAppendWaves * 64) void append_mfma_kernel(
+struct AppendCfg {
+    static constexpr int CB = GP / 32;                  // 32-wide output blocks
+    static constexpr int KPB = GP <= 96 ? 64 : 32;      // k per batch
+    static constexpr int RL = KPB * 2;                  // tile row bytes
+    static constexpr int CPR = RL / 16;                 // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;                // rows per load instruction
+    static constexpr int SWS = CPR == 8 ? 1 : 2;        // rows sharing a 256-byte bank window: 2^SWS
+    static constexpr int XI = 32 / RPI;                 // x load instructions per batch
+    static constexpr int EI = GP / RPI;                 // E load instructions per batch
+    static constexpr int KS = KPB / 16;                 // MFMA k-steps per batch
+    static constexpr int NB = 2;                        // slots per wave
+    static constexpr int SLOT = (32 + GP) * RL;         // bytes per slot
+    static constexpr int LDS = kAppendWaves * NB * SLOT;
+    static_assert(LDS + 0 <= 160 * 1024, "ring fits LDS");
+    static_assert(32 * (GP + 1) * 4 <= LDS, "the epilogue's sums fit the ring");
+};
+
+template <int GP>
+__device__ inline int append_swz(int row) {
+    using A = AppendCfg<GP>;
+    return (row >> A::SWS) & (A::CPR - 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int GP>
+__global__ __launch_bounds__(kAppendWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void append_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ E, uint8_t *__restrict__ codes,
     int64_t n, int C, int G, float shift) {
-    constexpr int CB = GP / 32;
+    using A = AppendCfg<GP>;
+    constexpr int CB = A::CB, KPB = A::KPB, RL = A::RL, CPR = A::CPR, RPI = A::RPI;
+    constexpr int XI = A::XI, EI = A::EI, KS = A::KS, NB = A::NB, SLOT = A::SLOT;
     constexpr int ROW = GP + 1;
-    __shared__ float U[32 * ROW];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // s_waitcnt immediate (gfx9 layout): vmcnt <= XI + EI, expcnt and lgkmcnt not waited on
+    constexpr int kWaitLoads = XI + EI;
+    static_assert(kWaitLoads < 64, "vmcnt field");
+    constexpr int kWaitOneSlot = (kWaitLoads & 0xF) | (0x7 << 4) | (0xF << 8) | ((kWaitLoads >> 4) << 14);
+    __shared__ __attribute__((aligned(16))) uint8_t ring[A::LDS];
+    float *U = reinterpret_cast<float *>(ring);   // the epilogue's sums, after the ring is drained
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t tile0 = (int64_t)blockIdx.x * 32;
     const int rows = (n - tile0) < 32 ? (int)(n - tile0) : 32;
     const int r = lane & 31, hh = lane >> 5;
     floatx16 acc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[cb] = floatx16{};
-    const uint16_t *xrow = x + (size_t)(tile0 + (r < rows ? r : 0)) * C;
-    const int nks = (C + 15) / 16;
-    for (int ks = wave; ks < nks; ks += kAppendWaves) {
-        const int k = ks * 16 + hh * 8;
-        const bool kin = k < C;
-        const u32x4 av = (kin && r < rows) ? *reinterpret_cast<const u32x4 *>(xrow + k) : u32x4{};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+    bool ein[CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int g = cb * 32 + r;
-            const u32x4 ev = (kin && g < G) ? *reinterpret_cast<const u32x4 *>(E + (size_t)g * C + k)
-                                            : u32x4{};
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, ev),
-                                                              acc[cb], 0, 0, 0);
+    for (int cb = 0; cb < CB; ++cb) ein[cb] = cb * 32 + r < G;
+    uint8_t *myring = ring + wave * NB * SLOT;
+
+    const int nbatch = (C + KPB - 1) / KPB;
+    const int nbw = nbatch > wave ? (nbatch - wave + kAppendWaves - 1) / kAppendWaves : 0;
+    // the row and 16-byte chunk this lane moves in each load instruction
+    const int lrow = lane / CPR, lslot = lane % CPR;
+    auto issue = [&](int s, int jw) {
+        const int kb = (wave + kAppendWaves * jw) * KPB;
+        uint8_t *xs = myring + s * SLOT, *es = xs + 32 * RL;
+#pragma unroll
+        for (int j = 0; j < XI; ++j) {
+            const int row = j * RPI + lrow;
+            const int k = kb + 8 * (lslot ^ append_swz<GP>(row));
+            const uint16_t *src = x + (size_t)(tile0 + (row < rows ? row : rows - 1)) * C + (k < C ? k : 0);
+            __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(xs + j * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < EI; ++j) {
+            const int row = j * RPI + lrow;
+            const int k = kb + 8 * (lslot ^ append_swz<GP>(row));
+            const uint16_t *src = E + (size_t)(row < G ? row : G - 1) * C + (k < C ? k : 0);
+            __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(es + j * 1024), 16, 0, 0);
+        }
+    };
+    auto compute = [&](int s, int jw) {
+        const int kb = (wave + kAppendWaves * jw) * KPB;
+        const bool jin = jw < nbw;   // batches past this wave's last contribute zero
+        const uint8_t *xs = myring + s * SLOT, *es = xs + 32 * RL;
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            const int c = 2 * i + hh;
+            const bool kin = jin && kb + 8 * c < C;
+            u32x4 av = *reinterpret_cast<const u32x4 *>(xs + r * RL + 16 * (c ^ append_swz<GP>(r)));
+            av = (kin && r < rows) ? av : u32x4{};
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int er = cb * 32 + r;
+                u32x4 ev = *reinterpret_cast<const u32x4 *>(es + er * RL + 16 * (c ^ append_swz<GP>(er)));
+                ev = (kin && ein[cb]) ? ev : u32x4{};
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                  __builtin_bit_cast(bf16x8, ev), acc[cb], 0,
+                                                                  0, 0);
+            }
+        }
+    };
+    // Straight-line steady state: slot s holds batch j0 + s; after its MFMAs
+    // have read it, the slot is refilled with batch j0 + s + NB (batches past
+    // the last are fetched from the last batch's addresses and zeroed in use).
+    if (nbw > 0) {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) issue(s, s < nbw ? s : nbw - 1);
+        for (int j0 = 0; j0 < nbw; j0 += NB) {
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+                // slot s holds the oldest of the NB batches in flight: wait until
+                // at most one slot's loads (the next batch's) are outstanding
+                __builtin_amdgcn_s_waitcnt(kWaitOneSlot);
+                compute(s, j0 + s);
+                const int jn = j0 + s + NB;
+                issue(s, jn < nbw ? jn : nbw - 1);
+            }
         }
     }
+    __syncthreads();   // every wave is done with its ring before it becomes U
     // fixed-order sum of the 4 waves' partial products in LDS
     for (int w = 0; w < kAppendWaves; ++w) {
         if (wave == w) {
