@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--timing-steps", type=int, default=5,
                     help="eager steps whose split-K launches are bracketed by HIP events")
     ap.add_argument("--no-append", action="store_true", help="skip the prefill-append measurement")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only the prefill-append measurement (with --eager: 12 eager calls)")
     ap.add_argument("--two-call", action="store_true",
                     help="per layer fsq_append + fsq_decode_attn instead of fsq_decode_step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -182,10 +184,10 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
     return m, ms, call_ms, replicas
 
 
-def append_prefill(w, torch, calls=40):
+def append_prefill(w, torch, calls=40, eager=False):
     """fsq_append of the workload's prefill chunk (x [n, C] -> codes [n, P]), replayed
-    from a HIP graph over replicas of x that together exceed the Infinity Cache;
-    returns the average time per call and its HBM roofline."""
+    from a HIP graph (or launched eagerly) over replicas of x that together exceed
+    the Infinity Cache; returns the average time per call and its HBM roofline."""
     import fsq_latent_decode_amd as fsq
     n = w.append_tokens
     E, _ = synth.layer_weights(w, 0)
@@ -203,15 +205,21 @@ def append_prefill(w, torch, calls=40):
             fsq.fsq_append(xs[r], Ed, codes[r])
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    def all_calls():
         for i in range(calls):
             fsq.fsq_append(xs[i % reps], Ed, codes[i % reps])
-    g.replay()
+    if eager:
+        run = all_calls
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            all_calls()
+        run = g.replay
+    run()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    g.replay()
+    run()
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / calls
@@ -223,7 +231,9 @@ def append_prefill(w, torch, calls=40):
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "bytes_per_call": nbytes,
                          "mfma_frac": flops / (us * 1e-6) / (MFMA_FP16_PEAK_TFLOPS * 1e12)},
-            "timing": f"{calls} calls in one HIP graph over {reps} replicas of x, events around the replay"}
+            "traffic": traffic_from_append_profile(w),
+            "timing": (f"{calls} eager calls" if eager else f"{calls} calls in one HIP graph")
+                      + f" over {reps} replicas of x, events around them"}
 
 
 def copy_probe(torch, mib):
@@ -326,6 +336,27 @@ def traffic_from_profile(w):
         return None
 
 
+def traffic_from_append_profile(w):
+    """HBM bytes per prefill-append launch from the committed counter summary, if it
+    was taken on the current append kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"append_prefill_traffic_{w.name}.txt")
+    src = os.path.join(ROOT, "fsq_latent_decode_amd", "csrc", "append.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("append_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def summarize(w, ms, call_ms, replicas):
     lens = synth.seq_lens(w)
     ctx = float(np.sum(lens))
@@ -358,6 +389,12 @@ def main():
     import torch
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
+        return
+    if args.append_only:
+        name = next(n for n in [args.workload] + [s for s in args.also.split(",") if s]
+                    if synth.WORKLOADS[n].append_tokens)
+        print(json.dumps(append_prefill(synth.WORKLOADS[name], torch, calls=12 if args.eager else 40,
+                                        eager=args.eager)))
         return
     w = synth.WORKLOADS[args.workload]
     m, ms, call_ms, reps = run_workload(w, torch, args.steps, args.warmup, args.eager,
