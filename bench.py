@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_g256", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--also", default="qwen3_8b_g84",
+    ap.add_argument("--also", default="qwen3_8b_g84,qwen3_1p7b_ragged,qwen3_8b_g84_1m",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -97,13 +97,17 @@ class Model:
         def bf(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+        fsq_codes = self.fsq_cache(w, torch, bf) if w.codes_from_fsq else None
         base = []
         for l in range(w.layers):
             E, W = synth.layer_weights(w, l)
-            codes = synth.layer_codes(w, l, lens=self.lens_np if w.ragged else None)
+            if fsq_codes is not None:
+                codes = fsq_codes.clone()
+            else:
+                codes = torch.from_numpy(synth.layer_codes(w, l, lens=self.lens_np if w.ragged else None)).to(dev)
             base.append(dict(E=bf(E), W=bf(W), q=bf(synth.layer_query(w, l)),
-                             x=bf(synth.layer_x(w, l, w.batch, synth.T_XNEW)),
-                             codes=torch.from_numpy(codes).to(dev)))
+                             x=bf(synth.layer_x(w, l, w.batch, synth.T_XNEW)), codes=codes))
+        del fsq_codes
         self.reps = [base]
         for _ in range(replicas - 1):
             self.reps.append([{k: v.clone() for k, v in d.items()} for d in base])
@@ -112,6 +116,24 @@ class Model:
                 d["out"] = torch.empty((w.batch, w.n_q, w.d_h), dtype=torch.bfloat16, device=dev)
         self.ws = fsq.alloc_workspace(w.batch, w.n_q, w.G, self.cap, dev)
         torch.cuda.synchronize()
+
+    def fsq_cache(self, w, torch, bf, chunk=8192):
+        """A cache whose codes are FSQ(E x) (the million-token workload): layer 0's
+        prefill chunks appended through fsq_append, x ~ N(0,1) bf16 drawn per
+        chunk by torch's seeded generator on the device; the layers get copies
+        (timing does not depend on the code values)."""
+        E, _ = synth.layer_weights(w, 0)
+        Ed = bf(E)
+        codes = torch.empty((w.batch, w.context, w.P), dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1_000_003 * w.wid + 7)
+        for b in range(w.batch):
+            for t0 in range(0, w.context, chunk):
+                n = min(chunk, w.context - t0)
+                x = torch.randn((n, w.C), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                self.fsq.fsq_append(x, Ed, codes[b, t0:t0 + n])
+        torch.cuda.synchronize()
+        return codes
 
     def step(self, r, ev=None, two_call=False):
         """One decode step over replica r: per layer, one fsq_decode_step call
