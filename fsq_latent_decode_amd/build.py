@@ -30,6 +30,10 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
            # keep hipcc from emitting packed-fp32 VALU forms
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in ordinary VGPRs: the decode kernels rescale
+           # their accumulators with VALU ops, and with accumulation registers
+           # the compiler copies every accumulator across each loop iteration
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"),
            "-o", tmp] + [os.path.join(PKG, s) for s in SOURCES]
     res = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)

@@ -57,8 +57,6 @@ __device__ inline int append_swz(int row) {
     return (row >> A::SWS) & (A::CPR - 1);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 template <int GP>
 __global__ __launch_bounds__(kAppendWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void append_mfma_kernel(

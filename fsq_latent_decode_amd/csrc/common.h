@@ -15,11 +15,14 @@ constexpr float kDelta = 0.5f;
 constexpr int kCodeOffset = 8;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;   // LDS pointer of direct-to-LDS loads
+typedef __attribute__((address_space(1))) void glb_void_t;   // global pointer of direct-to-LDS loads
 
 __host__ __device__ inline int bytes_per_token(int G) { return (G + 1) / 2; }
 __host__ __device__ inline int round_up(int a, int b) { return (a + b - 1) / b * b; }

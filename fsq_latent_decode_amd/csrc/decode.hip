@@ -84,7 +84,8 @@ __device__ inline void bf16_vec_to_f32(const typename VecT<VW>::T &v, float *f) 
 template <int VW>
 __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
-                                   int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale) {
+                                   int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
+                                   float odd_scale) {
     using A = AbsorbCfg<VW>;
     using VT = typename VecT<VW>::T;
     __shared__ float qs[kAbsorbHeads][kMaxDh];
@@ -159,7 +160,8 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
                 float sum = 0.0f;
                 for (int r = 0; r < A::DG; ++r) sum += red[r][j][col];
                 const int h = g * grp + hb + j;
-                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP)] = (_Float16)(k < G ? sum * scale : 0.0f);
+                const float sk = (k & 1) ? scale * odd_scale : scale;
+                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP)] = (_Float16)(k < G ? sum * sk : 0.0f);
             }
         }
         __syncthreads();
@@ -172,12 +174,13 @@ template <int VW>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict__ q,
                                                      const uint16_t *__restrict__ W_kv,
                                                      _Float16 *__restrict__ qt, int G, int GP,
-                                                     int n_q, int nqp, int n_kv, int d_h, float scale) {
+                                                     int n_q, int nqp, int n_kv, int d_h, float scale,
+                                                     float odd_scale) {
     const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
     int r = blockIdx.x;
     const int g = r % n_kv;
     r /= n_kv;
-    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
+    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale);
 }
 
 // ---------------------------------------------------------- decode step
@@ -199,7 +202,8 @@ __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int
                                                         const uint16_t *__restrict__ q,
                                                         const uint16_t *__restrict__ W_kv,
                                                         _Float16 *__restrict__ qt, int G, int GP,
-                                                        int n_q, int nqp, int n_kv, int d_h, float scale) {
+                                                        int n_q, int nqp, int n_kv, int d_h, float scale,
+                                                        float odd_scale) {
     const int bx = blockIdx.x;
     const int P = bytes_per_token(G);
     if (bx < n_app) {
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int
         int r = bx - n_app;
         const int g = r % n_kv;
         r /= n_kv;
-        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale);
+        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale);
     }
 }
 
@@ -218,8 +222,8 @@ template <int NT>
 static void launch_step_prep_nt(int vw, dim3 grid, hipStream_t st, const StepAppend &ap,
                                 const int32_t *seq_lens, int64_t seq_cap, int batch, int n_app,
                                 const uint16_t *q, const uint16_t *W_kv, _Float16 *qt, int G, int GP,
-                                int n_q, int nqp, int n_kv, int d_h, float scale) {
-#define FSQ_PREP_ARGS ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale
+                                int n_q, int nqp, int n_kv, int d_h, float scale, float odd_scale) {
+#define FSQ_PREP_ARGS ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale
     switch (vw) {
         case 8: step_prep_kernel<NT, 8><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
         case 4: step_prep_kernel<NT, 4><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
@@ -514,6 +518,415 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     }
 }
 
+// ----------------------------------------------------------- streaming split
+// Codes of one packed dword as fp16 operands with five operations: nibbles at
+// bits 4..7 of each 16-bit half are masked in place rather than shifted down,
+// so the operand order is (c0,c4) (16 c1,16 c5) (c2,c6) (16 c3,16 c7) - the
+// order of unpack_codes with odd coordinates (or, for a transposed read, odd
+// source rows) 16 times larger; the other operand carries a factor 1/16 there.
+__device__ inline half8 unpack_codes_x16(uint32_t w) {
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, w8 = w >> 8;
+    const u32x4 t = {w & lo, w & hi, w8 & lo, w8 & hi};
+    return __builtin_bit_cast(half8, t);
+}
+
+// The split kernel above makes its waves agree on one softmax state per round,
+// which costs three barriers and an fp16 copy of every tile in LDS per round;
+// that is the right trade when a CTA covers one or two rounds (short caches,
+// where launch and dependent latency dominate), not when it streams many.
+// decode_stream_kernel is the variant for long chunks. Each wave is an
+// independent flash-decoding unit over the tiles k = wave, wave + NW, ... of
+// the CTA's chunk with its own (m, l, acc) for all 32 heads and all GP latent
+// coordinates; the waves combine once, at the end of the chunk. Per tile:
+//   1. global -> LDS: the tile's packed bytes (one contiguous range of the
+//      sequence) arrive by 16-byte direct-to-LDS loads into a ring of D slots
+//      per wave, issued D - 1 tiles ahead, so each wave keeps D - 1 tiles of
+//      codes in flight without holding them in registers;
+//   2. scores: each lane reads its half of its token's row from the slot,
+//      unpacks to fp16 operands (codes as subnormals, see unpack_codes), and
+//      the waves' MFMAs compute all 32 heads' scores (K = latent coordinates);
+//   3. the same packed half-rows are written, still as nibbles, to a per-wave
+//      tile whose rows are 8-byte aligned and padded to an odd number of
+//      8-byte units;
+//   4. pooling: ds_read_b64_tr_b4 transposes 16 x 16 nibble blocks of that
+//      tile, so a lane receives 16 tokens of one latent coordinate, which is
+//      the operand layout of the pooling MFMA (K = tokens). The tokens behind
+//      the 16 nibbles are chosen (through the tile's row order) to be exactly
+//      the tokens whose probabilities the lane already holds from step 2, so
+//      no probability crosses lanes.
+// LDS traffic per code byte: DMA write 1, row read 1, tile write 1, transposed
+// read 1 (the split kernel moves 8: an fp16 copy written and read back).
+// Pooled sums come out in natural coordinate order.
+template <int GP, int NW, int D, bool AL>
+struct StreamCfg {
+    static constexpr int KB = GP / 16;                 // score k-blocks = dwords per lane half
+    static constexpr int CB = GP / 32;                 // pooling coordinate blocks
+    static constexpr int RB = GP / 2;                  // bytes of a token's row window
+    static constexpr int TS = RB + 8;                  // nibble-tile row stride: an odd number of 8-byte units
+    static constexpr int NEED = AL ? 32 * RB : 32 * RB + 32;   // a tile's bytes + alignment slack + read overrun
+    static constexpr int SLOTB = NEED < 1024 ? 1024 : (NEED + 127) / 128 * 128;
+    static constexpr int NI = (SLOTB + 1023) / 1024;   // direct-to-LDS loads per tile (64 lanes x 16 B)
+    static constexpr int RING = NW * D * SLOTB;
+    static constexpr int TILE = NW * 32 * TS;
+    static constexpr int QST = 32 * (GP + 8) * 2;      // Q~ staging, prologue only (aliases the tiles)
+    static constexpr int CBYTES = NW * 64 * 16 * 4;    // one coordinate block of every wave's sums
+    static constexpr int BPP0 = RING / CBYTES;
+    static constexpr int BPP = BPP0 < 1 ? 1 : (BPP0 > CB ? CB : BPP0);   // blocks per combine pass
+    static constexpr int COMB = BPP * CBYTES;          // the combine reuses the ring
+    static constexpr int RINGA = RING > COMB ? RING : COMB;
+    static_assert(QST <= TILE, "Q~ staging must fit in the tile region");
+    static_assert((D - 1) * NI < 64, "vmcnt field");
+    static_assert(KB % 2 == 0 && (!AL || KB % 4 == 0), "row halves in whole 8 / 16-byte units");
+};
+
+// Byte offset inside a ring slot of logical byte L of the tile: 16-byte chunks
+// are XOR-permuted inside each 128-byte line by the line index, so that the
+// same chunk of 8 consecutive 128-byte rows falls on distinct LDS banks.
+// The permutation is its own inverse.
+__device__ inline int slot_phys(int L) { return L ^ (((L >> 7) & 7) << 4); }
+
+// Row of token r (0..31) in the nibble tile: the 16 tokens a transposed read
+// gathers for one lane half are rows 16 hh .. 16 hh + 15.
+__device__ inline int tile_row(int r) { return ((r >> 3) << 2) | (r & 3) | (((r >> 2) & 1) << 4); }
+
+typedef int v2i32 __attribute__((vector_size(8)));
+
+// N transposed nibble reads (ds_read_b64_tr_b4) at LDS byte address a + 16 i,
+// issued back to back and waited for in the same asm block. Written in asm
+// because the compiler makes the builtin form wait for every direct-to-LDS
+// load in flight (to any LDS object), which would drain the code ring.
+// Result i: lane l of a 16-lane group receives nibble (l & 15) of the 8 bytes
+// that lane 16 (l / 16) + d of the group addresses, as nibble d (d = 0..15).
+template <int N>
+__device__ __attribute__((always_inline)) inline void tr4_reads(uint32_t a, v2i32 (&v)[N]);
+template <>
+__device__ __attribute__((always_inline)) inline void tr4_reads<1>(uint32_t a, v2i32 (&v)[1]) {
+    asm volatile("ds_read_b64_tr_b4 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a) : "memory");
+}
+template <>
+__device__ __attribute__((always_inline)) inline void tr4_reads<2>(uint32_t a, v2i32 (&v)[2]) {
+    asm volatile("ds_read_b64_tr_b4 %0, %2\n\tds_read_b64_tr_b4 %1, %2 offset:16\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(a) : "memory");
+}
+template <>
+__device__ __attribute__((always_inline)) inline void tr4_reads<3>(uint32_t a, v2i32 (&v)[3]) {
+    asm volatile("ds_read_b64_tr_b4 %0, %3\n\tds_read_b64_tr_b4 %1, %3 offset:16\n\t"
+                 "ds_read_b64_tr_b4 %2, %3 offset:32\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a) : "memory");
+}
+template <>
+__device__ __attribute__((always_inline)) inline void tr4_reads<4>(uint32_t a, v2i32 (&v)[4]) {
+    asm volatile("ds_read_b64_tr_b4 %0, %4\n\tds_read_b64_tr_b4 %1, %4 offset:16\n\t"
+                 "ds_read_b64_tr_b4 %2, %4 offset:32\n\tds_read_b64_tr_b4 %3, %4 offset:48\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
+}
+template <int N>
+__device__ __attribute__((always_inline)) inline void tr4_reads(uint32_t a, v2i32 (&v)[N]) {
+    static_assert(N > 4 && N <= 8, "1..8 reads");
+    v2i32 lo[4], hi[N - 4];
+    tr4_reads<4>(a, lo);
+    tr4_reads<N - 4>(a + 64, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = lo[i];
+#pragma unroll
+    for (int i = 0; i < N - 4; ++i) v[4 + i] = hi[i];
+}
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its global loads (__syncthreads would also wait for the
+// direct-to-LDS loads in flight, draining the ring) nor its global stores.
+__device__ __attribute__((always_inline)) inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int GP, int NW, int D, bool AL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 128 ? 2 : 3))) void decode_stream_kernel(
+    const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
+    const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
+    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S) {
+    using C = StreamCfg<GP, NW, D, AL>;
+    constexpr int KB = C::KB, CB = C::CB, TS = C::TS, SLOTB = C::SLOTB, NI = C::NI;
+    constexpr float kRescaleSlack = 8.0f;   // as in the split kernel: p <= 256
+    // s_waitcnt immediates (gfx9 layout), only vmcnt waited on
+    constexpr int kWaitAhead = (((D - 1) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 1) * NI) >> 4) << 14);
+    constexpr int kWaitAll = (0x7 << 4) | (0xF << 8);
+    // The ring (the only target of direct-to-LDS loads) and the nibble tiles are
+    // distinct LDS objects, so the compiler's waits for those loads do not
+    // extend to the tile stores.
+    __shared__ __attribute__((aligned(16))) uint8_t ring_lds[C::RINGA];
+    __shared__ __attribute__((aligned(16))) uint8_t tile_lds[C::TILE];
+    __shared__ float ms[NW][32], ls[NW][32];
+
+    const int P = (G + 1) / 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int64_t c0 = (int64_t)s * chunk;   // < seq_cap: the grid has ceil(seq_cap / chunk) chunks
+    // until the sequence length arrives, tiles are bounded by the cache capacity
+    int64_t cend = (c0 + chunk < seq_cap) ? c0 + chunk : seq_cap;
+    const int t = lane & 31, hh = lane >> 5;
+    const uint8_t *seq = codes + (size_t)b * seq_cap * P;
+    uint8_t *ring = ring_lds + wave * D * SLOTB;
+    uint8_t *tile = tile_lds + wave * 32 * TS;
+
+    auto tiles_before = [&](int64_t e) -> int {   // this wave's tiles starting before token e
+        const int64_t first = c0 + (int64_t)kTile * wave;
+        return e <= first ? 0 : (int)((e - first + (int64_t)kTile * NW - 1) / ((int64_t)kTile * NW));
+    };
+    auto tile_t0 = [&](int j) -> int64_t { return c0 + (int64_t)kTile * (wave + NW * j); };
+    // direct-to-LDS loads of tile j (which starts before cend) into slot j % D:
+    // NI loads of 64 x 16 bytes; the last load's window is moved back to end at
+    // the slot's end (overlapping windows write the same bytes), and chunks
+    // past the tile's last byte repeat that byte's chunk
+    auto issue = [&](int j) {
+        int64_t t0 = tile_t0(j);
+        int64_t rem = cend - t0;
+        if (rem <= 0) {   // prologue only: a tile past the chunk re-reads its first row
+            t0 = c0;
+            rem = 1;
+        }
+        const int n = rem < kTile ? (int)rem : kTile;
+        const uintptr_t A = (uintptr_t)(seq + (size_t)t0 * P);
+        const uintptr_t a0 = A & ~(uintptr_t)15;
+        const uintptr_t last = (A + (uintptr_t)n * P - 1) & ~(uintptr_t)15;
+        uint8_t *slot = ring + (j % D) * SLOTB;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int pb = (i * 1024 < SLOTB - 1024) ? i * 1024 : SLOTB - 1024;
+            uintptr_t src = a0 + (uintptr_t)slot_phys(pb + 16 * lane);
+            src = src < last ? src : last;
+            __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(slot + pb), 16, 0, 0);
+        }
+    };
+
+    // Q~ rows of this head group -> LDS (rows padded to GP + 8 halves) -> each
+    // lane's B operands, as in the split kernel. Only the first tile is loaded
+    // alongside (the compiler waits for all loads before the Q~ stores); the
+    // ring's other D - 2 tiles are issued once Q~ is in place.
+    issue(0);
+    half8 qv[KB];
+    {
+        constexpr int QROW = GP + 8;
+        _Float16 *qsm = reinterpret_cast<_Float16 *>(tile_lds);   // the tiles are free here
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
+        constexpr int NQ16 = 32 * GP / 8;
+        constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
+        u32x4 qreg[NQI];
+#pragma unroll
+        for (int u = 0; u < NQI; ++u) {
+            const int i = threadIdx.x + u * NW * 64;
+            qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < NQI; ++u) {
+            // threads past the last chunk rewrite it with the same data (no
+            // branch, so the loads stay ahead of the ring's)
+            const int i0 = threadIdx.x + u * NW * 64, i = i0 < NQ16 ? i0 : NQ16 - 1;
+            const int r = i / (GP / 8), c = i - r * (GP / 8);
+            *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
+        }
+        lds_barrier();
+        int64_t T = seq_lens[b];
+        T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
+        if (c0 >= T) {   // uniform: nothing to do; no load may still target the LDS
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+            return;
+        }
+        cend = (c0 + chunk < T) ? c0 + chunk : T;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            qv[kb] = *reinterpret_cast<const half8 *>(qsm + t * QROW + 16 * kb + 8 * hh);
+        lds_barrier();   // before the tile region is reused
+    }
+    const int nt = tiles_before(cend);
+#pragma unroll
+    for (int j = 1; j < D - 1; ++j) issue(j);   // a static number of loads (see issue)
+
+    float m_ref = -INFINITY, l_run = 0.0f;
+    floatx16 acc[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[j] = floatx16{};
+
+    // transposed-read source row of this lane: nibble d of the result is token
+    // row (16 hh + (d & 8) + sigma^-1(d & 7)); see the unpack order
+    const int dsrc = lane & 15;
+    const int rsrc = 16 * hh + (dsrc & 8) + (((dsrc & 3) << 1) | ((dsrc >> 2) & 1));
+    const uint8_t *trsrc = tile + rsrc * TS + 8 * ((lane >> 4) & 1);
+    const uint32_t tr_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)trsrc;
+    uint8_t *tdst = tile + tile_row(t) * TS + hh * (GP / 4);
+
+    for (int j = 0; j < nt; ++j) {
+        const bool ahead = j + D - 1 < nt;
+        if (ahead) issue(j + D - 1);   // into the slot tile j - 1 used
+        if (ahead)
+            __builtin_amdgcn_s_waitcnt(kWaitAhead);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+        const int64_t t0 = tile_t0(j);
+        const int64_t rem = cend - t0;
+        const int ntok = rem < kTile ? (int)rem : kTile;
+        const uint8_t *slot = ring + (j % D) * SLOTB;
+
+        // ---- this lane's half of token t's row (GP / 4 bytes) -> KB dwords.
+        // Rows past the tile's tokens and padding coordinates G..GP-1 hold
+        // finite codes (stale slot bytes or the next row's): the former get
+        // probability 0, the latter meet zero q~ entries and are never read back.
+        uint32_t cur[KB];
+        if (AL) {
+#pragma unroll
+            for (int i = 0; i < KB / 4; ++i) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + slot_phys(t * P + hh * (GP / 4) + 16 * i));
+                cur[4 * i + 0] = v.x;
+                cur[4 * i + 1] = v.y;
+                cur[4 * i + 2] = v.z;
+                cur[4 * i + 3] = v.w;
+            }
+        } else {
+            const int mis = (int)((uintptr_t)(seq + (size_t)t0 * P) & 15);
+            const int a = mis + t * P + hh * (GP / 4);
+            const int a0 = a & ~3, sh = (a & 3) * 8;
+            uint32_t ld[KB + 1];
+#pragma unroll
+            for (int i = 0; i < KB + 1; ++i) ld[i] = *reinterpret_cast<const uint32_t *>(slot + slot_phys(a0 + 4 * i));
+#pragma unroll
+            for (int i = 0; i < KB; ++i) cur[i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
+        }
+#pragma unroll
+        for (int i = 0; i < KB / 2; ++i)
+            *reinterpret_cast<uint2 *>(tdst + 8 * i) = uint2{cur[2 * i], cur[2 * i + 1]};
+
+        // ---- scores of the tile's 32 tokens for the 32 heads (units of 2^-24)
+        floatx16 sc = floatx16{};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[kb]), qv[kb], sc, 0, 0, 0);
+
+        // ---- online softmax of this wave (lane: head t, tokens tok(r))
+        float sv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = sc[r];
+        if (ntok < kTile) {   // the chunk's last tile only (uniform)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tok = (r >> 2) * 8 + hh * 4 + (r & 3);
+                sv[r] = tok < ntok ? sv[r] : -INFINITY;
+            }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kCodeScale;
+        const bool bump = tmax > m_ref + kRescaleSlack;
+        const float m_new = bump ? tmax : m_ref;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+        const bool rescale = bump && m_ref != -INFINITY;
+        m_ref = m_new;
+        // weights p in fp16, pairwise; the normaliser sums exactly those fp16
+        // values (v_dot2 with (1, 1) accumulates in fp32)
+        half2 ph[8];
+        float psum = 0.0f;
+        const half2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i], kCodeScale, -m_new));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i + 1], kCodeScale, -m_new));
+            ph[i] = half2{(_Float16)e0, (_Float16)e1};
+            psum = __builtin_amdgcn_fdot2(ph[i], one2, psum, false);
+        }
+        l_run = l_run * alpha + psum;
+        if (__any(rescale)) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+        }
+        // pooling B operands: K slots 2, 3, 6, 7 meet codes read 16x (odd
+        // source rows of the transposed read), so their weights are scaled by 1/16
+        const half2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const half2 q1 = ph[1] * s16, q3 = ph[3] * s16, q5 = ph[5] * s16, q7 = ph[7] * s16;
+        const half8 pv0 = {ph[0].x, ph[0].y, q1.x, q1.y, ph[2].x, ph[2].y, q3.x, q3.y};
+        const half8 pv1 = {ph[4].x, ph[4].y, q5.x, q5.y, ph[6].x, ph[6].y, q7.x, q7.y};
+
+        // ---- pooling: acc[cb][coordinate 32 cb + m][head] += z^T p
+        v2i32 zt[CB];
+        tr4_reads<CB>(tr_addr, zt);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zt[cb][0]), pv0, acc[cb], 0, 0, 0);
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zt[cb][1]), pv1, acc[cb], 0, 0, 0);
+        }
+    }
+
+    // ---- combine the waves: M = max m_w, c_w = 2^(m_w - M), L = sum c_w l_w,
+    // zbar = 2^24 sum c_w acc_w / L - 8, summed in wave order
+    __builtin_amdgcn_s_waitcnt(kWaitAll);   // prologue loads past the length may be in flight
+    lds_barrier();                          // every wave is done with its ring and tile
+    const float l_w = l_run + __shfl_xor(l_run, 32);
+    if (lane < 32) {
+        ms[wave][lane] = m_ref;
+        ls[wave][lane] = l_w;
+    }
+    lds_barrier();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ms[w][t]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mw = ms[w][t];
+        L += mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * ls[w][t];
+    }
+    const float cw = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float zscale = kCodeScale / L;
+    const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
+    const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
+    floatx4 *cbuf = reinterpret_cast<floatx4 *>(ring_lds);   // [block][wave][4][64 lanes]
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int p0 = 0; p0 < CB; p0 += C::BPP) {
+#pragma unroll
+        for (int i = 0; i < C::BPP; ++i) {
+            if (p0 + i < CB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    cbuf[((i * NW + wave) * 4 + e) * 64 + lane] =
+                        floatx4{acc[p0 + i][4 * e], acc[p0 + i][4 * e + 1], acc[p0 + i][4 * e + 2],
+                                acc[p0 + i][4 * e + 3]} * cw;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < C::BPP; ++i) {
+            const int cb = p0 + i;
+            if (cb < CB && cb % NW == wave) {
+                floatx4 sum[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum[e] = cbuf[((i * NW + 0) * 4 + e) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum[e] += cbuf[((i * NW + w) * 4 + e) * 64 + lane];
+                if (t < heads) {
+                    _Float16 *dst = part_z + (pbase + t) * GP + cb * 32 + hh * 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const half4 v = {(_Float16)fmaf(sum[e][0], zscale, -8.0f),
+                                         (_Float16)fmaf(sum[e][1], zscale, -8.0f),
+                                         (_Float16)fmaf(sum[e][2], zscale, -8.0f),
+                                         (_Float16)fmaf(sum[e][3], zscale, -8.0f)};
+                        *reinterpret_cast<half4 *>(dst + 8 * e) = v;
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    }
+    if (wave == 0 && lane < heads) {
+        part_ml[(pbase + lane) * 2 + 0] = M;
+        part_ml[(pbase + lane) * 2 + 1] = L;
+    }
+}
+
 // ----------------------------------------------------------------- merge
 // One CTA per (head, sequence): M = max_i m_i, c_i = l_i 2^(m_i - M),
 // zbar = sum_i c_i zbar_i / sum_i c_i, out = W_v,g zbar. Every global load (the
@@ -527,7 +940,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
-    int chunk, int S) {
+    int chunk, int S, int natural) {
     using VT = typename VecT<VW>::T;
     // W_v vectors per thread held in registers (two or more threads per row);
     // narrow vectors (odd G) beyond 32 per thread are read in the dot loop
@@ -646,7 +1059,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     for (int p = tid; p < GP; p += blockDim.x) {
         float z = 0.0f;
         for (int u = 0; u < SG; ++u) z += zpart[u * GP + p];
-        zbar[pos_to_coord(p, GP)] = z * invL;
+        zbar[natural ? p : pos_to_coord(p, GP)] = z * invL;
     }
     __syncthreads();
 
@@ -702,11 +1115,40 @@ static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, cons
     return hipGetLastError();
 }
 
+template <int GP, int D>
+static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
+                                  const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
+                                  int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
+    constexpr int NW = kStreamWaves;
+    dim3 grid(pl.S, batch, pl.nqp / 32);
+    dim3 block(NW * 64);
+    // 16-byte row reads when every token row starts on a 16-byte boundary and a
+    // lane half is whole 16-byte chunks
+    constexpr bool kCanAl = GP % 64 == 0;
+    const bool al = kCanAl && G == GP && ((uintptr_t)codes & 15) == 0;
+    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl> : decode_stream_kernel<GP, NW, D, false>;
+    if (ev0 && ev1)
+        hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
+                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S);
+    else
+        k<<<grid, block, 0, st>>>(qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, pl.nqp, pl.chunk,
+                                  pl.S);
+    return hipGetLastError();
+}
+
 template <int GP>
 static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
                                const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
                                hipEvent_t ev1) {
+    if (pl.stream) {
+        if (pl.waves != kStreamWaves) return hipErrorInvalidValue;
+        constexpr int D = GP >= 128 ? 3 : 4;   // stream_depth(GP)
+        if (stream_depth(GP) != D) return hipErrorInvalidValue;
+        return launch_stream_d<GP, D>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st,
+                                      ev0, ev1);
+    }
     if (pl.waves != split_waves(GP)) return hipErrorInvalidValue;
     return launch_split_nw<GP, (GP >= 128 ? 8 : 4)>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
                                                     batch, st, ev0, ev1);
@@ -722,6 +1164,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
     _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
     float *pml = reinterpret_cast<float *>(ws + pl.off_ml);
     const float scale = 1.4426950408889634f / sqrtf((float)d_h);
+    // the streaming kernel reads odd coordinates' codes 16x (unpack_codes_x16)
+    const float odd = pl.stream ? 0.0625f : 1.0f;
     hipError_t e;
     // widest bf16 vector that divides G and the W_kv alignment
     const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
@@ -736,7 +1180,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
         const dim3 grid((unsigned)(n_app + n_abs));
 #define FSQ_PREP_CALL(NT) \
-    launch_step_prep_nt<NT>(vw, grid, st, ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale)
+    launch_step_prep_nt<NT>(vw, grid, st, ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd)
         switch (nt) {
             case 1: FSQ_PREP_CALL(1); break;
             case 2: FSQ_PREP_CALL(2); break;
@@ -749,10 +1193,10 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
         const dim3 ag((unsigned)n_abs);
         switch (vw) {
-            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
-            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
-            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale); break;
-            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale);
+            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
+            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
+            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
+            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -777,7 +1221,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         if (e != hipSuccess) return e;
     }
     const dim3 mg(n_q, batch);
-#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S
+#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S, pl.stream
     switch (vw) {
         case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
         case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;

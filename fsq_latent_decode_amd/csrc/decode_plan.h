@@ -17,12 +17,23 @@ constexpr int kMaxNq = 64;     // largest number of query heads
 // waves x 32 tokens.
 inline int split_waves(int GP) { return GP >= 128 ? 8 : 4; }
 
+// Streaming split (long chunks): 4-wave CTAs, each wave keeping stream_depth - 1
+// tiles of codes in flight. Registers and LDS allow two CTAs per CU when
+// GP >= 128 and three below, so 512 or 768 CTAs (one resident set) are aimed
+// for. It is chosen when every wave gets at least kStreamMinTiles tiles of 32
+// tokens.
+constexpr int kStreamWaves = 4;
+constexpr int kStreamMinTiles = 4;
+inline int stream_depth(int GP) { return GP >= 128 ? 3 : 4; }
+inline int stream_target(int GP) { return GP >= 128 ? 512 : 768; }
+
 struct DecodePlan {
     int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
     int nqp = 0;      // n_q padded to a multiple of 32 (head groups)
     int chunk = 0;    // tokens per split
     int S = 0;        // splits per sequence (0 when seq_cap == 0)
     int waves = 0;    // waves per split-K CTA
+    int stream = 0;   // 1: decode_stream_kernel (partials in natural coordinate order)
     size_t off_qt = 0, off_acc = 0, off_ml = 0, total = 0;
 };
 
@@ -32,10 +43,16 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
     DecodePlan p;
     p.GP = (G + 31) / 32 * 32;
     p.nqp = (n_q + 31) / 32 * 32;
-    p.waves = split_waves(p.GP);
+    const int64_t work = int64_t(batch) * seq_cap;
+    const int squant = 32 * kStreamWaves;
+    const int starget = stream_target(p.GP);
+    int64_t sper = (work + starget - 1) / starget;
+    sper = (sper + squant - 1) / squant * squant;
+    p.stream = sper >= (int64_t)kStreamMinTiles * squant ? 1 : 0;
+    p.waves = p.stream ? kStreamWaves : split_waves(p.GP);
     const int quantum = 32 * p.waves;
-    const int target = p.waves == 8 ? 256 : 512;
-    int64_t per = (int64_t(batch) * seq_cap + target - 1) / target;
+    const int target = p.stream ? starget : (p.waves == 8 ? 256 : 512);
+    int64_t per = (work + target - 1) / target;
     if (per < quantum) per = quantum;
     per = (per + quantum - 1) / quantum * quantum;
     if (per > (int64_t)1 << 30) per = (int64_t)1 << 30;
