@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--also", default="qwen3_8b_g84,qwen3_1p7b_ragged,qwen3_8b_g84_1m",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sdpa", action="store_true",
+                    help="skip the PyTorch SDPA comparison on materialised K/V")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=5,
@@ -379,6 +381,136 @@ def traffic_from_append_profile(w):
         return None
 
 
+def sdpa_comparison(w, torch, fsq_ms, steps=10, warmup=3):
+    """The same decode step over materialised bf16 K = Z W_k^T and V = Z W_v^T
+    (4 * n_kv * d_h bytes per token and layer) through PyTorch's fused SDPA,
+    timed like the FSQ steps (HIP graph of all layers, inputs resident). The
+    query heads of a kv head ride as rows of one attention (GQA without copies).
+    Only PyTorch's flash / memory-efficient backends are allowed; if neither
+    takes these shapes the comparison reports why instead of running the
+    unfused path. The layer-0 output is compared with fsq_decode_attn's on the
+    same codes."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import fsq_latent_decode_amd as fsq
+    if w.ragged or w.codes_from_fsq:
+        return None
+    lens = synth.seq_lens(w)
+    T = int(lens[0])
+    grp = w.n_q // w.n_kv
+    to_bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    layers = []
+    for l in range(w.layers):
+        _, Wb = synth.layer_weights(w, l)
+        codes = torch.from_numpy(synth.layer_codes(w, l)).cuda()          # [B, T, P]
+        z = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(w.batch, T, -1)[..., :w.G]
+        z = z.float() - 8.0                                                # [B, T, G]
+        Wf = to_bf(Wb).float()
+        Wk = Wf[: w.n_kv * w.d_h].reshape(w.n_kv, w.d_h, w.G)
+        Wv = Wf[w.n_kv * w.d_h:].reshape(w.n_kv, w.d_h, w.G)
+        zz = z.unsqueeze(1)                                                # [B, 1, T, G] fp32
+        K = torch.matmul(zz, Wk.transpose(1, 2).contiguous().unsqueeze(0)).to(torch.bfloat16).contiguous()
+        V = torch.matmul(zz, Wv.transpose(1, 2).contiguous().unsqueeze(0)).to(torch.bfloat16).contiguous()
+        qb = to_bf(synth.layer_query(w, l))                                # [B, n_q, d_h]
+        q = qb.reshape(w.batch, w.n_kv, grp, w.d_h).contiguous()
+        layers.append(dict(q=q, q1=qb.reshape(w.batch, w.n_q, 1, w.d_h).contiguous(), K=K, V=V, qb=qb,
+                           W=to_bf(Wb), codes=codes))
+        del z, zz, Wf
+    backends = [SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]
+    kv_bytes = w.layers * w.batch * T * 4 * w.n_kv * w.d_h
+    res = {"workload": w.name, "kv_bytes_per_token_per_layer": 4 * w.n_kv * w.d_h,
+           "fsq_bytes_per_token_per_layer": w.P, "kv_bytes_per_step": kv_bytes,
+           "materialised_hbm_roofline_ms": kv_bytes / (HBM_PEAK_GBS * 1e9) * 1e3,
+           "fsq_ms_per_step": fsq_ms, "backends_allowed": "flash, memory-efficient", "forms": {}}
+    best = None
+    for form in ("grouped_rows", "enable_gqa", "matmul_softmax"):
+        r = _time_sdpa(torch, F, sdpa_kernel, backends, layers, form, steps, warmup)
+        res["forms"][form] = r
+        if "ms_per_step" in r and (best is None or r["ms_per_step"] < res["forms"][best]["ms_per_step"]):
+            best = form
+    if best is None:
+        return res
+    ms = res["forms"][best]["ms_per_step"]
+    ach = kv_bytes / (ms * 1e-3) / 1e9
+    d0 = layers[0]
+    mine = torch.empty((w.batch, w.n_q, w.d_h), dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn(d0["qb"], d0["codes"], d0["W"], torch.from_numpy(lens).cuda(), mine, w.n_kv)
+    torch.cuda.synchronize()
+    a = res["forms"][best].pop("_out0").reshape(w.batch, w.n_q, w.d_h).double()
+    for r in res["forms"].values():
+        r.pop("_out0", None)
+    b = mine.double()
+    res.update({"best_form": best, "ms_per_step": ms,
+                "context_tokens_per_s": float(np.sum(lens)) / (ms * 1e-3),
+                "achieved_GBs": ach, "hbm_frac": ach / HBM_PEAK_GBS, "fsq_speedup": ms / fsq_ms,
+                "layer0_rel_l2_sdpa_vs_fsq": float(torch.linalg.norm(a - b) / torch.linalg.norm(b))})
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def _time_sdpa(torch, F, sdpa_kernel, backends, layers, form, steps, warmup):
+    """Time one step of attention calls over all layers; form "grouped_rows"
+    puts the query heads of a kv head as rows of one SDPA call, "enable_gqa"
+    passes all query heads with PyTorch's GQA flag, "matmul_softmax" is
+    unfused: bf16 library products S = K q^T and out = P^T V (contiguous
+    operands) around an fp32 softmax over the whole context."""
+    res = {}
+    outs = []
+    for d in layers:
+        outs.append(torch.empty_like(d["q"] if form != "enable_gqa" else d["q1"]))
+        if form == "matmul_softmax":
+            d["qT"] = d["q"].transpose(-1, -2).contiguous()                 # [B, n_kv, d_h, grp]
+    scale = 1.0 / math.sqrt(layers[0]["q"].shape[-1])
+
+    def step():
+        for d, o in zip(layers, outs):
+            if form == "grouped_rows":
+                o.copy_(F.scaled_dot_product_attention(d["q"], d["K"], d["V"]))
+            elif form == "enable_gqa":
+                o.copy_(F.scaled_dot_product_attention(d["q1"], d["K"], d["V"], enable_gqa=True))
+            else:
+                sc = torch.matmul(d["K"], d["qT"]).float() * scale          # [B, n_kv, T, grp]
+                p = torch.softmax(sc, dim=2).to(torch.bfloat16)
+                o.copy_(torch.matmul(p.transpose(-1, -2).contiguous(), d["V"]))
+
+    try:
+        with sdpa_kernel(backends):
+            step()
+            torch.cuda.synchronize()
+            graph = None
+            try:
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    step()
+                torch.cuda.current_stream().wait_stream(s)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    step()
+            except Exception as e:  # noqa: BLE001 - fall back to eager launches
+                graph = None
+                res["graph_error"] = str(e)[:200]
+            run = graph.replay if graph is not None else step
+            for _ in range(warmup):
+                run()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                run()
+            t1.record()
+            torch.cuda.synchronize()
+    except RuntimeError as e:
+        res["unavailable"] = str(e)[:300]
+        return res
+    res.update({"ms_per_step": t0.elapsed_time(t1) / steps,
+                "timing": ("HIP graph of all layers" if "graph_error" not in res else "eager launches")
+                          + f", {steps} steps", "_out0": outs[0]})
+    return res
+
+
 def summarize(w, ms, call_ms, replicas):
     lens = synth.seq_lens(w)
     ctx = float(np.sum(lens))
@@ -433,6 +565,13 @@ def main():
         also[name] = summarize(w2, ms2, cm2, reps2)
         del m2
         torch.cuda.empty_cache()
+    sdpa = {}
+    if not args.no_sdpa:
+        fsq_ms = {w.name: main_res["ms_per_step"], **{k: v["ms_per_step"] for k, v in also.items()}}
+        for name in [args.workload] + [s for s in args.also.split(",") if s]:
+            r = sdpa_comparison(synth.WORKLOADS[name], torch, fsq_ms[name])
+            if r is not None:
+                sdpa[name] = r
     app = None
     for name in [args.workload] + [s for s in args.also.split(",") if s]:
         if synth.WORKLOADS[name].append_tokens and not args.no_append:
@@ -463,6 +602,7 @@ def main():
         "cpu_baseline": cpu,
         "also": also,
         "append_prefill": app,
+        "sdpa_comparison": sdpa,
     }
     print(json.dumps(line))
 
