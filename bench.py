@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true",
                     help="skip the PyTorch SDPA comparison on materialised K/V")
+    ap.add_argument("--no-recon", action="store_true",
+                    help="skip the key-reconstruction comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=5,
@@ -136,6 +138,13 @@ class Model:
                 self.fsq.fsq_append(x, Ed, codes[b, t0:t0 + n])
         torch.cuda.synchronize()
         return codes
+
+    def step_recon(self, r):
+        """One decode step through the key-reconstruction variant (no append)."""
+        fsq, w = self.fsq, self.w
+        for d in self.reps[r]:
+            fsq.fsq_decode_attn_recon(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv,
+                                      workspace=self.ws)
 
     def step(self, r, ev=None, two_call=False):
         """One decode step over replica r: per layer, one fsq_decode_step call
@@ -511,6 +520,57 @@ def _time_sdpa(torch, F, sdpa_kernel, backends, layers, form, steps, warmup):
     return res
 
 
+def recon_comparison(w, torch, fsq_ms, steps=10, warmup=3):
+    """The decode step with keys rebuilt per tile (fsq_decode_attn_recon) on the
+    same replicated inputs, graph-replayed like the FSQ steps. The path is bound
+    by its MFMA work: 2 n_kv d_h G flops per token for the keys, against the
+    absorbed path's 2 n_q G for the scores (pooling and W_v are common)."""
+    if w.d_h % 32 or w.d_h > 128:
+        return None
+    lens = synth.seq_lens(w)
+    per_step_bytes = w.layers * decode_call_bytes(w, lens)
+    replicas = min(8, max(2, math.ceil(4 * MALL_BYTES / per_step_bytes)))
+    m = Model(w, torch, replicas)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for r in range(replicas):
+            m.step_recon(r)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(replicas):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            m.step_recon(r)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % replicas].replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[(warmup + i) % replicas].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ctx = float(np.sum(lens))
+    key_flops = 2.0 * w.layers * ctx * w.n_kv * w.d_h * w.G
+    common = 2.0 * w.layers * ctx * w.n_q * (w.d_h + w.G)     # scores on rebuilt keys + pooling
+    flops = key_flops + common
+    absorbed = 2.0 * w.layers * ctx * w.n_q * w.G * 2
+    tf = flops / (ms * 1e-3) / 1e12
+    del m, graphs
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_per_step": ms, "context_tokens_per_s": ctx / (ms * 1e-3),
+            "fsq_ms_per_step": fsq_ms, "slowdown_vs_absorbed": ms / fsq_ms,
+            "flops_per_step": flops, "absorbed_path_flops_per_step": absorbed,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_FP16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / MFMA_FP16_PEAK_TFLOPS,
+                         "t_roof_ms": flops / (MFMA_FP16_PEAK_TFLOPS * 1e12) * 1e3},
+            "timing": f"{steps} steps from HIP graphs over {replicas} replicas (no append)"}
+
+
 def summarize(w, ms, call_ms, replicas):
     lens = synth.seq_lens(w)
     ctx = float(np.sum(lens))
@@ -572,6 +632,16 @@ def main():
             r = sdpa_comparison(synth.WORKLOADS[name], torch, fsq_ms[name])
             if r is not None:
                 sdpa[name] = r
+    recon = {}
+    if not args.no_recon:
+        fsq_ms = {w.name: main_res["ms_per_step"], **{k: v["ms_per_step"] for k, v in also.items()}}
+        for name in [args.workload] + [s for s in args.also.split(",") if s]:
+            w2 = synth.WORKLOADS[name]
+            if w2.ragged or w2.codes_from_fsq:
+                continue
+            r = recon_comparison(w2, torch, fsq_ms[name])
+            if r is not None:
+                recon[name] = r
     app = None
     for name in [args.workload] + [s for s in args.also.split(",") if s]:
         if synth.WORKLOADS[name].append_tokens and not args.no_append:
@@ -603,6 +673,7 @@ def main():
         "also": also,
         "append_prefill": app,
         "sdpa_comparison": sdpa,
+        "recon_comparison": recon,
     }
     print(json.dumps(line))
 

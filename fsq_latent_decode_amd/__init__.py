@@ -15,7 +15,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
-           "fsq_decode_attn_timed", "fsq_decode_step")
+           "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                       vp, sz, vp]
         L.fsq_decode_step.restype = ctypes.c_int
+        L.fsq_decode_attn_recon.argtypes = L.fsq_decode_attn.argtypes
+        L.fsq_decode_attn_recon.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -182,6 +184,22 @@ def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, se
     else:
         ev = [_event_handle(e) for e in split_events]
         _check(lib().fsq_decode_attn_timed(*args, ev[0], ev[1]), "fsq_decode_attn_timed")
+    return out
+
+
+def fsq_decode_attn_recon(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor,
+                          seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int,
+                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fsq_decode_attn computed with keys rebuilt per tile (K = Z W_k^T) instead of
+    absorbed queries: the measured comparison. Same arguments and workspace."""
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, G, cap, q.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    rc = lib().fsq_decode_attn_recon(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(),
+                                     seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, cap,
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc, "fsq_decode_attn_recon")
     return out
 
 

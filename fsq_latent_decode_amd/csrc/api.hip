@@ -12,6 +12,10 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, const uint16_t *x_new,
                          const uint16_t *E, int C);
+hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
+                               const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
+                               int batch, int n_q, int n_kv, int d_h, int G, int64_t seq_cap,
+                               void *workspace, hipStream_t st);
 }  // namespace fsq
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -99,6 +103,26 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
     }
     return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
                          workspace_bytes, stream, nullptr, nullptr, x_new, E, C);
+}
+
+int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
+    if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
+    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > 128 || d_h % 32 != 0 || n_q / n_kv > 32)
+        return FSQ_ERR_UNSUPPORTED;
+    if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
+    if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
+    if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
+    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
+    if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u))
+        return FSQ_ERR_WORKSPACE;
+    if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
+    hipError_t e = fsq::launch_decode_recon(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h,
+                                            G, seq_cap, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -641,13 +641,28 @@ __device__ __attribute__((always_inline)) inline void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int GP, int NW, int D, bool AL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 128 ? 2 : 3))) void decode_stream_kernel(
+// Inputs of the key-reconstruction variant (RC): instead of absorbed queries,
+// each CTA serves the heads of one kv head g and rebuilds the tile's keys
+// K = Z W_k,g^T (d_h <= 128, d_h % 32 == 0) before scoring them against q.
+struct ReconArgs {
+    const uint16_t *q, *W_kv;
+    int n_kv, d_h;
+    float scale;
+};
+constexpr int kReconMaxDh = 128;
+
+template <int GP, int NW, int D, bool AL, bool RC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 3)))) void decode_stream_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
-    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S) {
+    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S,
+    ReconArgs ra) {
     using C = StreamCfg<GP, NW, D, AL>;
     constexpr int KB = C::KB, CB = C::CB, TS = C::TS, SLOTB = C::SLOTB, NI = C::NI;
+    // scores arrive in units of 2^-24 from absorbed queries (codes as fp16
+    // subnormals), in plain log2 units from rebuilt keys (rescaled below)
+    constexpr float kSS = RC ? 1.0f : kCodeScale;
+    constexpr int WROW = GP + 8;   // rebuilt-key operand rows (halves), RC only
     constexpr float kRescaleSlack = 8.0f;   // as in the split kernel: p <= 256
     // s_waitcnt immediates (gfx9 layout), only vmcnt waited on
     constexpr int kWaitAhead = (((D - 1) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 1) * NI) >> 4) << 14);
@@ -657,6 +672,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
     // extend to the tile stores.
     __shared__ __attribute__((aligned(16))) uint8_t ring_lds[C::RINGA];
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[C::TILE];
+    __shared__ __attribute__((aligned(16))) _Float16 wk_lds[RC ? kReconMaxDh * WROW : 8];
     __shared__ float ms[NW][32], ls[NW][32];
 
     const int P = (G + 1) / 2;
@@ -706,8 +722,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
     // alongside (the compiler waits for all loads before the Q~ stores); the
     // ring's other D - 2 tiles are issued once Q~ is in place.
     issue(0);
-    half8 qv[KB];
-    {
+    half8 qv[RC ? 1 : KB];
+    half8 qb[RC ? 4 : 1][2];   // RC: B operands q[head][d] * scale per 32-row block of d and half
+    const int grp = RC ? n_q / ra.n_kv : 32;
+    if constexpr (RC) {
+        // W_k,g (bf16, [d_h][G]) -> fp16 rows of WROW halves in operand order,
+        // odd coordinates scaled 1/16 (they meet codes read 16x); zero past G
+        const int g = hg, DB = ra.d_h / 32;
+        const uint16_t *wk = ra.W_kv + (size_t)g * ra.d_h * G;
+        for (int it = threadIdx.x; it < ra.d_h * (GP / 8); it += NW * 64) {
+            const int d = it / (GP / 8), Dw = it - d * (GP / 8);   // 8 coordinates 8 Dw .. 8 Dw + 7
+            half8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 8 * Dw + e;
+                const float x = c < G ? bf16_to_f32(wk[(size_t)d * G + c]) : 0.0f;
+                v[((e & 3) << 1) | (e >> 2)] = (_Float16)((e & 1) ? x * 0.0625f : x);
+            }
+            *reinterpret_cast<half8 *>(wk_lds + d * WROW + 16 * (Dw % KB) + 8 * (Dw / KB)) = v;
+        }
+        // q operands: lane = head n of this kv head, K slot (hh, jj) of block
+        // (db, e) = d 32 db + (2 e + jj / 4) 8 + 4 hh + jj % 4
+        // (lanes past the group's heads and blocks past d_h read in-bounds
+        // elements and zero them)
+        const bool hv = t < grp;
+        const uint16_t *qh = ra.q + ((size_t)b * n_q + (size_t)g * grp + (hv ? t : 0)) * ra.d_h;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int d = 32 * db + (2 * e + (jj >> 2)) * 8 + 4 * hh + (jj & 3);
+                    const bool ok = hv && db < DB;
+                    const float x = bf16_to_f32(qh[ok ? d : 0]) * ra.scale;
+                    qb[db][e][jj] = (_Float16)(ok ? x : 0.0f);
+                }
+        lds_barrier();
+        int64_t T = seq_lens[b];
+        T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
+        if (c0 >= T) {   // uniform: nothing to do; no load may still target the LDS
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+            return;
+        }
+        cend = (c0 + chunk < T) ? c0 + chunk : T;
+    } else {
         constexpr int QROW = GP + 8;
         _Float16 *qsm = reinterpret_cast<_Float16 *>(tile_lds);   // the tiles are free here
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
@@ -799,9 +858,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
 
         // ---- scores of the tile's 32 tokens for the 32 heads (units of 2^-24)
         floatx16 sc = floatx16{};
+        if constexpr (!RC) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[kb]), qv[kb], sc, 0, 0, 0);
+            for (int kb = 0; kb < KB; ++kb)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[kb]), qv[kb], sc, 0, 0, 0);
+        } else {
+            // rebuilt keys: K^T[d][token] = sum_c W_k[d][c] code_c (in units of
+            // 2^-24; the code offset adds 8 rowsum_d, a per-head constant of the
+            // score that cancels in the softmax), then scores K q
+            half8 zb[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) zb[kb] = unpack_codes_x16(cur[kb]);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                if (db < ra.d_h / 32) {
+                    floatx16 kt = floatx16{};
+                    const _Float16 *wr = wk_lds + (32 * db + t) * WROW + 8 * hh;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        kt = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const half8 *>(wr + 16 * kb),
+                                                                    zb[kb], kt, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        half8 ka;
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) ka[jj] = (_Float16)(kt[8 * e + jj] * kCodeScale);
+                        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[db][e], sc, 0, 0, 0);
+                    }
+                }
+            }
+        }
 
         // ---- online softmax of this wave (lane: head t, tokens tok(r))
         float sv[16];
@@ -817,7 +903,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
         float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kCodeScale;
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kSS;
         const bool bump = tmax > m_ref + kRescaleSlack;
         const float m_new = bump ? tmax : m_ref;
         const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
@@ -830,8 +916,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
         const half2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i], kCodeScale, -m_new));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i + 1], kCodeScale, -m_new));
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i], kSS, -m_new));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * i + 1], kSS, -m_new));
             ph[i] = half2{(_Float16)e0, (_Float16)e1};
             psum = __builtin_amdgcn_fdot2(ph[i], one2, psum, false);
         }
@@ -878,8 +964,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GP >= 1
     }
     const float cw = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
     const float zscale = kCodeScale / L;
-    const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
-    const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
+    const int heads = RC ? grp : ((n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32);
+    const size_t pbase = ((size_t)b * S + s) * n_q + hg * (RC ? grp : 32);
     floatx4 *cbuf = reinterpret_cast<floatx4 *>(ring_lds);   // [block][wave][4][64 lanes]
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -1127,13 +1213,32 @@ static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, cons
     // lane half is whole 16-byte chunks
     constexpr bool kCanAl = GP % 64 == 0;
     const bool al = kCanAl && G == GP && ((uintptr_t)codes & 15) == 0;
-    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl> : decode_stream_kernel<GP, NW, D, false>;
+    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl, false> : decode_stream_kernel<GP, NW, D, false, false>;
+    const ReconArgs ra{};
     if (ev0 && ev1)
         hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
-                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S);
+                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S, ra);
     else
         k<<<grid, block, 0, st>>>(qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, pl.nqp, pl.chunk,
-                                  pl.S);
+                                  pl.S, ra);
+    return hipGetLastError();
+}
+
+// Key-reconstruction variant: grid (chunks, sequences, kv heads), chunk and
+// split count from recon_split (at most the plan's split count, so the same
+// workspace holds the partials).
+template <int GP>
+static hipError_t launch_recon(int chunk, int S, const uint8_t *codes, const int32_t *seq_lens,
+                               _Float16 *pz, float *pml, int64_t seq_cap, int G, int n_q, int batch,
+                               const ReconArgs &ra, hipStream_t st) {
+    constexpr int NW = kStreamWaves;
+    constexpr int D = GP >= 128 ? 3 : 4;
+    dim3 grid(S, batch, ra.n_kv);
+    dim3 block(NW * 64);
+    constexpr bool kCanAl = GP % 64 == 0;
+    const bool al = kCanAl && G == GP && ((uintptr_t)codes & 15) == 0;
+    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl, true> : decode_stream_kernel<GP, NW, D, false, true>;
+    k<<<grid, block, 0, st>>>(nullptr, codes, seq_lens, pz, pml, seq_cap, G, n_q, 0, chunk, S, ra);
     return hipGetLastError();
 }
 
@@ -1222,6 +1327,61 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
     }
     const dim3 mg(n_q, batch);
 #define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S, pl.stream
+    switch (vw) {
+        case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        case 2: decode_merge_kernel<2><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
+        default: decode_merge_kernel<1><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS);
+    }
+#undef FSQ_MERGE_ARGS
+    return hipGetLastError();
+}
+
+// The key-reconstruction comparison: no absorption launch; the split kernel
+// rebuilds keys per tile, then the same merge applies W_v once.
+hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
+                               const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
+                               int batch, int n_q, int n_kv, int d_h, int G, int64_t seq_cap,
+                               void *workspace, hipStream_t st) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
+    float *pml = reinterpret_cast<float *>(ws + pl.off_ml);
+    // about 512 CTAs over (chunks, sequences, kv heads); chunks no shorter than
+    // the plan's, so the split count (and the partials) fit its workspace
+    const int64_t quantum = 32 * kStreamWaves;
+    int64_t per = ((int64_t)batch * n_kv * seq_cap + 511) / 512;
+    per = (per + quantum - 1) / quantum * quantum;
+    int64_t chunk = per > pl.chunk ? per : pl.chunk;
+    const int S = seq_cap > 0 ? (int)((seq_cap + chunk - 1) / chunk) : 0;
+    const ReconArgs ra{q, W_kv, n_kv, d_h, 1.4426950408889634f / sqrtf((float)d_h)};
+    hipError_t e = hipSuccess;
+    if (S > 0) {
+        switch (pl.GP) {
+#define FSQ_RECON_CASE(X)                                                                               \
+    case X:                                                                                             \
+        e = launch_recon<X>((int)chunk, S, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, ra, st); \
+        break;
+            FSQ_RECON_CASE(32)
+            FSQ_RECON_CASE(64)
+            FSQ_RECON_CASE(96)
+            FSQ_RECON_CASE(128)
+            FSQ_RECON_CASE(160)
+            FSQ_RECON_CASE(192)
+            FSQ_RECON_CASE(224)
+            FSQ_RECON_CASE(256)
+#undef FSQ_RECON_CASE
+            default:
+                return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+    }
+    const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
+                   : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
+                   : ((G & 1) == 0 && ((uintptr_t)W_kv & 3) == 0) ? 2
+                                                                   : 1;
+    const dim3 mg(n_q, batch);
+    const int chunk_i = S > 0 ? (int)chunk : pl.chunk;
+#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, chunk_i, (S > 0 ? S : 1), 1
     switch (vw) {
         case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
         case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;

@@ -170,6 +170,24 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
                     int32_t batch, int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
                     int64_t seq_cap, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fsq_decode_attn_recon - the same attention as fsq_decode_attn, computed the
+ * way the pages' kernel does: keys are rebuilt per 32-token tile on chip,
+ * K_tile = Z_tile W_k,g^T (Eq. 5 without key norm and RoPE), and scored against
+ * q; values are still pooled in latent space and decoded once (Eq. 6). Kept as
+ * a measured comparison of the absorbed path (about 2 n_kv d_h G flops per
+ * token for the keys instead of 2 n_q G); nothing is written to memory but the
+ * workspace and out. Same arguments, layouts and workspace size as
+ * fsq_decode_attn; results agree with it to fp16 rounding, not bit for bit.
+ * Sizes: as fsq_decode_attn, and d_h % 32 == 0, d_h <= 128, n_q / n_kv <= 32.
+ * Errors: as fsq_decode_attn; FSQ_ERR_UNSUPPORTED for the further size limits.
+ */
+int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                          const int32_t *seq_lens, uint16_t *out,
+                          int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                          int64_t seq_cap, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,6 +132,26 @@ def test_decode_step_validation_before_any_hip_call(args, status):
     assert rc == status
 
 
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    # (q, codes, W, lens, out, batch, n_q, n_kv, d_h, G, cap, ws, ws_bytes)
+    ((256, 256, 256, 256, 256, 0, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 1, 32, 6, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 80, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),   # d_h % 32
+    ((256, 256, 256, 256, 256, 1, 32, 8, 256, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),  # d_h > 128
+    ((256, 256, 256, 256, 256, 1, 64, 1, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),  # 64 heads per kv head
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 300, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((0, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 8, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256, 64), fsq.FSQ_ERR_WORKSPACE),
+    ((256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 0, 1 << 20), fsq.FSQ_ERR_WORKSPACE),
+])
+def test_decode_recon_validation_before_any_hip_call(args, status):
+    (q, c, w, l, o, B, nq, nkv, dh, G, cap, ws, wsb) = args
+    rc = fsq.lib().fsq_decode_attn_recon(q, c, w, l, o, B, nq, nkv, dh, G, cap, ws, wsb, None)
+    assert rc == status
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(fsq, "_lib", None)
     monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")

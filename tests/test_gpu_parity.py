@@ -205,6 +205,49 @@ def test_decode_stream_deterministic(fsq):
     assert np.array_equal(a, b)
 
 
+def run_decode_recon(fsq, q_bits, packed, W_bits, lens, n_kv):
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn_recon(q, dev_u8(packed), dev_bf16(W_bits),
+                              torch.from_numpy(np.asarray(lens, np.int32)).cuda(), out, n_kv)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# The key-reconstruction variant (keys rebuilt per tile instead of absorbed
+# queries) against the same oracle: short and long caches, odd G, every d_h it
+# takes (32..128), MQA and wide GQA groups, empty and one-token sequences.
+@pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens", [
+    (1, 16, 8, 128, 64, 1024, [1024]),
+    (1, 32, 8, 128, 256, 33, [33]),
+    (2, 32, 8, 128, 84, 1000, [1000, 257]),
+    (4, 16, 8, 128, 256, 600, [0, 1, 31, 600]),
+    (1, 8, 1, 64, 37, 130, [129]),
+    (3, 12, 4, 96, 96, 2100, [2100, 1500, 33]),
+    (1, 32, 8, 128, 160, 5000, [4999]),
+    (2, 16, 4, 32, 30, 300, [300, 7]),
+    (1, 32, 1, 128, 200, 700, [699]),
+    (2, 32, 8, 128, 256, 65536, [20000, 4097]),
+    (4, 32, 8, 128, 84, 65537, [65537, 1, 31, 33]),
+])
+def test_decode_recon_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
+    q, packed, W, lens = decode_case(G * 11 + cap, B, n_q, n_kv, d_h, G, cap, lens)
+    got = run_decode_recon(fsq, q, packed, W, lens, n_kv)
+    ref = oracle_decode(q, packed, W, lens, n_kv, G)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            e = rel_l2(got[b], ref[b])
+            assert e < REL_L2, (b, e)
+
+
+def test_decode_recon_deterministic(fsq):
+    q, packed, W, lens = decode_case(9, 2, 32, 8, 128, 84, 9000, [9000, 4097])
+    a = run_decode_recon(fsq, q, packed, W, lens, 8)
+    assert np.array_equal(a, run_decode_recon(fsq, q, packed, W, lens, 8))
+
+
 def test_decode_deterministic_and_split_invariant(fsq):
     q, packed, W, lens = decode_case(5, 2, 32, 8, 128, 84, 9000, [9000, 4097])
     a = run_decode(fsq, q, packed, W, lens, 8)
