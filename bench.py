@@ -139,12 +139,17 @@ class Model:
         torch.cuda.synchronize()
         return codes
 
-    def step_recon(self, r):
-        """One decode step through the key-reconstruction variant (no append)."""
+    def step_recon(self, r, rope=None):
+        """One decode step through the key-reconstruction variant (no append);
+        with rope = (gain, theta, eps), the Eq. 5 keys with norm and RoPE."""
         fsq, w = self.fsq, self.w
         for d in self.reps[r]:
-            fsq.fsq_decode_attn_recon(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv,
-                                      workspace=self.ws)
+            if rope is None:
+                fsq.fsq_decode_attn_recon(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv,
+                                          workspace=self.ws)
+            else:
+                fsq.fsq_decode_attn_rope(d["q"], d["codes"], d["W"], rope[0], self.lens, d["out"], w.n_kv,
+                                         rope[1], rope[2], workspace=self.ws)
 
     def step(self, r, ev=None, two_call=False):
         """One decode step over replica r: per layer, one fsq_decode_step call
@@ -520,29 +525,36 @@ def _time_sdpa(torch, F, sdpa_kernel, backends, layers, form, steps, warmup):
     return res
 
 
-def recon_comparison(w, torch, fsq_ms, steps=10, warmup=3):
-    """The decode step with keys rebuilt per tile (fsq_decode_attn_recon) on the
-    same replicated inputs, graph-replayed like the FSQ steps. The path is bound
-    by its MFMA work: 2 n_kv d_h G flops per token for the keys, against the
-    absorbed path's 2 n_q G for the scores (pooling and W_v are common)."""
-    if w.d_h % 32 or w.d_h > 128:
+def recon_comparison(w, torch, fsq_ms, steps=10, warmup=3, rope=False):
+    """The decode step with keys rebuilt per tile (fsq_decode_attn_recon; with
+    rope, fsq_decode_attn_rope: key RMS norm with a seeded gain, eps 1e-6, and
+    RoPE with theta 1e6) on the same replicated inputs, graph-replayed like the
+    FSQ steps. The path is bound by its MFMA work: 2 n_kv d_h G flops per token
+    for the keys, against the absorbed path's 2 n_q G for the scores (pooling
+    and W_v are common)."""
+    if w.d_h % 32 or w.d_h > 128 or (rope and w.d_h not in (64, 128)):
         return None
     lens = synth.seq_lens(w)
     per_step_bytes = w.layers * decode_call_bytes(w, lens)
     replicas = min(8, max(2, math.ceil(4 * MALL_BYTES / per_step_bytes)))
     m = Model(w, torch, replicas)
+    rp = None
+    if rope:
+        gam = synth.normal_bf16(synth.rng(w.wid, 0, 301), (w.d_h,), 0.1)
+        gam = synth.f32_to_bf16_bits(synth.bf16_bits_to_f64(gam).astype(np.float32) + 1.0)
+        rp = (torch.from_numpy(gam.view(np.int16)).view(torch.bfloat16).cuda(), 1e6, 1e-6)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         for r in range(replicas):
-            m.step_recon(r)
+            m.step_recon(r, rp)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     graphs = []
     for r in range(replicas):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            m.step_recon(r)
+            m.step_recon(r, rp)
         graphs.append(g)
     for i in range(warmup):
         graphs[i % replicas].replay()
@@ -562,7 +574,8 @@ def recon_comparison(w, torch, fsq_ms, steps=10, warmup=3):
     tf = flops / (ms * 1e-3) / 1e12
     del m, graphs
     torch.cuda.empty_cache()
-    return {"workload": w.name, "ms_per_step": ms, "context_tokens_per_s": ctx / (ms * 1e-3),
+    return {"workload": w.name, "keys": ("RoPE_t(N_k(W_k z)), theta 1e6, eps 1e-6" if rope else "W_k z"),
+            "ms_per_step": ms, "context_tokens_per_s": ctx / (ms * 1e-3),
             "fsq_ms_per_step": fsq_ms, "slowdown_vs_absorbed": ms / fsq_ms,
             "flops_per_step": flops, "absorbed_path_flops_per_step": absorbed,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_FP16_PEAK_TFLOPS,
@@ -642,6 +655,9 @@ def main():
             r = recon_comparison(w2, torch, fsq_ms[name])
             if r is not None:
                 recon[name] = r
+            r = recon_comparison(w2, torch, fsq_ms[name], rope=True)
+            if r is not None:
+                recon[name + "_rope"] = r
     app = None
     for name in [args.workload] + [s for s in args.also.split(",") if s]:
         if synth.WORKLOADS[name].append_tokens and not args.no_append:

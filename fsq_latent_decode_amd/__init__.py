@@ -15,7 +15,8 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
-           "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon")
+           "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
+           "fsq_decode_attn_rope")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_step.restype = ctypes.c_int
         L.fsq_decode_attn_recon.argtypes = L.fsq_decode_attn.argtypes
         L.fsq_decode_attn_recon.restype = ctypes.c_int
+        f32 = ctypes.c_float
+        L.fsq_decode_attn_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, f32,
+                                           vp, sz, vp]
+        L.fsq_decode_attn_rope.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -200,6 +205,28 @@ def fsq_decode_attn_recon(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tens
                                      seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, cap,
                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(rc, "fsq_decode_attn_recon")
+    return out
+
+
+def fsq_decode_attn_rope(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor,
+                         k_norm: torch.Tensor, seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int,
+                         rope_theta: float, norm_eps: float, workspace: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Decode with Eq. 5 keys in full: k^_t = RoPE_t(N_k(W_k z_t)) rebuilt per tile.
+    k_norm [d_h] bf16 is the key-norm gain; q is already normalised and rotated.
+    Other arguments as fsq_decode_attn."""
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
+    _dev(k_norm, "k_norm", torch.bfloat16, 1)
+    if k_norm.shape[0] != d_h:
+        raise ValueError(f"k_norm must be [{d_h}], got {tuple(k_norm.shape)}")
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, G, cap, q.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    rc = lib().fsq_decode_attn_rope(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), k_norm.data_ptr(),
+                                    seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, cap,
+                                    float(rope_theta), float(norm_eps), workspace.data_ptr(),
+                                    workspace.numel(), _stream(stream))
+    _check(rc, "fsq_decode_attn_rope")
     return out
 
 

@@ -15,7 +15,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
 hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                                const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
                                int batch, int n_q, int n_kv, int d_h, int G, int64_t seq_cap,
-                               void *workspace, hipStream_t st);
+                               void *workspace, hipStream_t st, const uint16_t *gamma, float eps,
+                               float theta);
 }  // namespace fsq
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -105,10 +106,11 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
                          workspace_bytes, stream, nullptr, nullptr, x_new, E, C);
 }
 
-int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
-                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
-                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+static int recon_common(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                        const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                        int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                        size_t workspace_bytes, void *stream, const uint16_t *gamma, float eps,
+                        float theta) {
     if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
     if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > 128 || d_h % 32 != 0 || n_q / n_kv > 32)
@@ -121,8 +123,31 @@ int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_
         return FSQ_ERR_WORKSPACE;
     if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     hipError_t e = fsq::launch_decode_recon(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h,
-                                            G, seq_cap, workspace, (hipStream_t)stream);
+                                            G, seq_cap, workspace, (hipStream_t)stream, gamma, eps,
+                                            theta);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
+}
+
+int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return recon_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
+                        workspace_bytes, stream, nullptr, 0.0f, 0.0f);
+}
+
+int fsq_decode_attn_rope(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                         const uint16_t *k_norm, const int32_t *seq_lens, uint16_t *out,
+                         int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                         int64_t seq_cap, float rope_theta, float norm_eps, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
+    if (!(rope_theta > 1.0f) || !(norm_eps >= 0.0f) || !(rope_theta < 1e30f) || !(norm_eps < 1.0f))
+        return FSQ_ERR_SHAPE;
+    if (d_h != 64 && d_h != 128) return FSQ_ERR_UNSUPPORTED;
+    if (!k_norm) return FSQ_ERR_NULL;
+    return recon_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
+                        workspace_bytes, stream, k_norm, norm_eps, rope_theta);
 }
 
 }  // extern "C"

@@ -641,17 +641,33 @@ __device__ __attribute__((always_inline)) inline void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Inputs of the key-reconstruction variant (RC): instead of absorbed queries,
-// each CTA serves the heads of one kv head g and rebuilds the tile's keys
-// K = Z W_k,g^T (d_h <= 128, d_h % 32 == 0) before scoring them against q.
+// Inputs of the key-reconstruction variants (RC = 1, 2): instead of absorbed
+// queries, each CTA serves the heads of one kv head g and rebuilds the tile's
+// keys K = Z W_k,g^T (d_h <= 128, d_h % 32 == 0) before scoring them against
+// q. RC = 2 also applies the rest of Eq. 5: the key RMS norm (gamma, eps) and
+// rotate-half RoPE at each key's cache position, with the rotation of channel
+// pair (i, i + d_h/2) for position t being t * rope_f[i] / 2^64 revolutions.
 struct ReconArgs {
     const uint16_t *q, *W_kv;
     int n_kv, d_h;
     float scale;
+    const uint16_t *gamma;   // RC = 2: [d_h] bf16
+    float eps;               // RC = 2
+    uint64_t rope_f[64];     // RC = 2: theta^(-2i/d_h) / (2 pi) in units of 2^-64, i < d_h/2
 };
 constexpr int kReconMaxDh = 128;
 
-template <int GP, int NW, int D, bool AL, bool RC>
+// Codes of one packed dword as fp16 levels n - 8 (exact) in the order of
+// unpack_codes: the nibble is placed under the exponent of 1024.0 and 1032 is
+// subtracted.
+__device__ inline half8 unpack_codes_centered(uint32_t w) {
+    const uint32_t m = 0x000F000Fu, e = 0x64006400u;
+    const u32x4 t = {(w & m) | e, ((w >> 4) & m) | e, ((w >> 8) & m) | e, ((w >> 12) & m) | e};
+    const _Float16 c = (_Float16)1032.0f;
+    return __builtin_bit_cast(half8, t) - half8{c, c, c, c, c, c, c, c};
+}
+
+template <int GP, int NW, int D, bool AL, int RC>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 3)))) void decode_stream_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
@@ -673,6 +689,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     __shared__ __attribute__((aligned(16))) uint8_t ring_lds[C::RINGA];
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[C::TILE];
     __shared__ __attribute__((aligned(16))) _Float16 wk_lds[RC ? kReconMaxDh * WROW : 8];
+    __shared__ float gam_lds[RC == 2 ? kReconMaxDh : 1];
+    __shared__ uint64_t rope_lds[RC == 2 ? kReconMaxDh / 2 : 1];
     __shared__ float ms[NW][32], ls[NW][32];
 
     const int P = (G + 1) / 2;
@@ -726,8 +744,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     half8 qb[RC ? 4 : 1][2];   // RC: B operands q[head][d] * scale per 32-row block of d and half
     const int grp = RC ? n_q / ra.n_kv : 32;
     if constexpr (RC) {
-        // W_k,g (bf16, [d_h][G]) -> fp16 rows of WROW halves in operand order,
-        // odd coordinates scaled 1/16 (they meet codes read 16x); zero past G
+        // W_k,g (bf16, [d_h][G]) -> fp16 rows of WROW halves in operand order
+        // (RC = 1: odd coordinates scaled 1/16, they meet codes read 16x); zero
+        // past G
         const int g = hg, DB = ra.d_h / 32;
         const uint16_t *wk = ra.W_kv + (size_t)g * ra.d_h * G;
         for (int it = threadIdx.x; it < ra.d_h * (GP / 8); it += NW * 64) {
@@ -737,9 +756,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
             for (int e = 0; e < 8; ++e) {
                 const int c = 8 * Dw + e;
                 const float x = c < G ? bf16_to_f32(wk[(size_t)d * G + c]) : 0.0f;
-                v[((e & 3) << 1) | (e >> 2)] = (_Float16)((e & 1) ? x * 0.0625f : x);
+                v[((e & 3) << 1) | (e >> 2)] = (_Float16)((RC == 1 && (e & 1)) ? x * 0.0625f : x);
             }
             *reinterpret_cast<half8 *>(wk_lds + d * WROW + 16 * (Dw % KB) + 8 * (Dw / KB)) = v;
+        }
+        if constexpr (RC == 2) {
+            for (int i = threadIdx.x; i < ra.d_h; i += NW * 64) gam_lds[i] = bf16_to_f32(ra.gamma[i]);
+            for (int i = threadIdx.x; i < ra.d_h / 2; i += NW * 64) rope_lds[i] = ra.rope_f[i];
         }
         // q operands: lane = head n of this kv head, K slot (hh, jj) of block
         // (db, e) = d 32 db + (2 e + jj / 4) 8 + 4 hh + jj % 4
@@ -863,26 +886,76 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
             for (int kb = 0; kb < KB; ++kb)
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[kb]), qv[kb], sc, 0, 0, 0);
         } else {
-            // rebuilt keys: K^T[d][token] = sum_c W_k[d][c] code_c (in units of
-            // 2^-24; the code offset adds 8 rowsum_d, a per-head constant of the
-            // score that cancels in the softmax), then scores K q
+            // rebuilt keys, 32-row blocks of K^T[d][token] = sum_c W_k[d][c] z_c;
+            // lane (token t, half hh) holds d = 32 db + (r/4) 8 + 4 hh + r%4.
+            // RC = 1: codes as subnormals (units of 2^-24, levels + 8: the
+            // offset adds 8 rowsum_d, a per-head score constant that cancels in
+            // the softmax). RC = 2: the levels themselves, as N_k needs them.
+            const int DB = ra.d_h / 32;
             half8 zb[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) zb[kb] = unpack_codes_x16(cur[kb]);
+            for (int kb = 0; kb < KB; ++kb)
+                zb[kb] = RC == 2 ? unpack_codes_centered(cur[kb]) : unpack_codes_x16(cur[kb]);
+            floatx16 kt[4];
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
-                if (db < ra.d_h / 32) {
-                    floatx16 kt = floatx16{};
+                kt[db] = floatx16{};
+                if (db < DB) {
                     const _Float16 *wr = wk_lds + (32 * db + t) * WROW + 8 * hh;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
-                        kt = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const half8 *>(wr + 16 * kb),
-                                                                    zb[kb], kt, 0, 0, 0);
+                        kt[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            *reinterpret_cast<const half8 *>(wr + 16 * kb), zb[kb], kt[db], 0, 0, 0);
+                }
+            }
+            if constexpr (RC == 2) {
+                // N_k: k * gamma / sqrt(mean(k^2) + eps) over the token's d_h
+                // channels (this lane's half, then the other half's sum)
+                float ss = 0.0f;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) ss = fmaf(kt[db][r], kt[db][r], ss);
+                ss += __shfl_xor(ss, 32);
+                const float inv = __builtin_amdgcn_rsqf(ss / (float)ra.d_h + ra.eps);
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int d = 32 * db + (r >> 2) * 8 + 4 * hh + (r & 3);
+                        kt[db][r] *= inv * gam_lds[d < ra.d_h ? d : 0];
+                    }
+                // RoPE_t on pairs (d, d + d_h/2): blocks db and db + DB/2, same r
+                // (d_h is 64 or 128, so DB is 2 or 4)
+                const uint64_t pos = (uint64_t)(t0 + t);
+                auto rot = [&](floatx16 &x, floatx16 &y, int db) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int d = 32 * db + (r >> 2) * 8 + 4 * hh + (r & 3);
+                        const uint64_t ph = pos * rope_lds[d];   // revolutions mod 1, units of 2^-64
+                        const float rev = (float)(uint32_t)(ph >> 40) * 5.9604645e-8f;   // 2^-24
+                        const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                        const float a = x[r], bb = y[r];
+                        x[r] = a * cs - bb * sn;
+                        y[r] = bb * cs + a * sn;
+                    }
+                };
+                if (DB == 4) {
+                    rot(kt[0], kt[2], 0);
+                    rot(kt[1], kt[3], 1);
+                } else {
+                    rot(kt[0], kt[1], 0);
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                if (db < DB) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         half8 ka;
 #pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) ka[jj] = (_Float16)(kt[8 * e + jj] * kCodeScale);
+                        for (int jj = 0; jj < 8; ++jj)
+                            ka[jj] = (_Float16)(RC == 1 ? kt[db][8 * e + jj] * kCodeScale : kt[db][8 * e + jj]);
                         sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[db][e], sc, 0, 0, 0);
                     }
                 }
@@ -1227,7 +1300,7 @@ static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, cons
 // Key-reconstruction variant: grid (chunks, sequences, kv heads), chunk and
 // split count from recon_split (at most the plan's split count, so the same
 // workspace holds the partials).
-template <int GP>
+template <int GP, int RC>
 static hipError_t launch_recon(int chunk, int S, const uint8_t *codes, const int32_t *seq_lens,
                                _Float16 *pz, float *pml, int64_t seq_cap, int G, int n_q, int batch,
                                const ReconArgs &ra, hipStream_t st) {
@@ -1237,7 +1310,7 @@ static hipError_t launch_recon(int chunk, int S, const uint8_t *codes, const int
     dim3 block(NW * 64);
     constexpr bool kCanAl = GP % 64 == 0;
     const bool al = kCanAl && G == GP && ((uintptr_t)codes & 15) == 0;
-    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl, true> : decode_stream_kernel<GP, NW, D, false, true>;
+    auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl, RC> : decode_stream_kernel<GP, NW, D, false, RC>;
     k<<<grid, block, 0, st>>>(nullptr, codes, seq_lens, pz, pml, seq_cap, G, n_q, 0, chunk, S, ra);
     return hipGetLastError();
 }
@@ -1342,7 +1415,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
 hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                                const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
                                int batch, int n_q, int n_kv, int d_h, int G, int64_t seq_cap,
-                               void *workspace, hipStream_t st) {
+                               void *workspace, hipStream_t st, const uint16_t *gamma, float eps,
+                               float theta) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
     float *pml = reinterpret_cast<float *>(ws + pl.off_ml);
@@ -1353,13 +1427,30 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
     per = (per + quantum - 1) / quantum * quantum;
     int64_t chunk = per > pl.chunk ? per : pl.chunk;
     const int S = seq_cap > 0 ? (int)((seq_cap + chunk - 1) / chunk) : 0;
-    const ReconArgs ra{q, W_kv, n_kv, d_h, 1.4426950408889634f / sqrtf((float)d_h)};
+    ReconArgs ra{};
+    ra.q = q;
+    ra.W_kv = W_kv;
+    ra.n_kv = n_kv;
+    ra.d_h = d_h;
+    ra.scale = 1.4426950408889634f / sqrtf((float)d_h);
+    ra.gamma = gamma;
+    ra.eps = eps;
+    if (gamma) {
+        // rotation rate of channel pair i in revolutions per position, as a
+        // 64-bit fraction: t * rope_f[i] mod 2^64 is the angle of position t
+        // without rounding growth in t
+        for (int i = 0; i < d_h / 2; ++i) {
+            const long double f = powl((long double)theta, -2.0L * i / d_h) / (2.0L * 3.141592653589793238462643383279L);
+            ra.rope_f[i] = (uint64_t)llroundl(ldexpl(f, 64));
+        }
+    }
     hipError_t e = hipSuccess;
     if (S > 0) {
         switch (pl.GP) {
-#define FSQ_RECON_CASE(X)                                                                               \
-    case X:                                                                                             \
-        e = launch_recon<X>((int)chunk, S, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, ra, st); \
+#define FSQ_RECON_CASE(X)                                                                                   \
+    case X:                                                                                                 \
+        e = gamma ? launch_recon<X, 2>((int)chunk, S, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, ra, st) \
+                  : launch_recon<X, 1>((int)chunk, S, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, ra, st); \
         break;
             FSQ_RECON_CASE(32)
             FSQ_RECON_CASE(64)

@@ -188,6 +188,33 @@ int fsq_decode_attn_recon(const uint16_t *q, const uint8_t *codes, const uint16_
                           int64_t seq_cap, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/*
+ * fsq_decode_attn_rope - one decode step with the keys of Eq. 5 in full,
+ * k^_t = RoPE_t(N_k(W_k,g z_t)), rebuilt per 32-token tile on chip (absorbing
+ * the query is not possible here: N_k is nonlinear and RoPE_t depends on t);
+ * values are pooled in latent space and decoded once (Eq. 6):
+ *   N_k(k)     = k * gamma / sqrt(mean_i k_i^2 + norm_eps)   (per key head)
+ *   RoPE_t(k)  : for i < d_h/2, with a = t * rope_theta^(-2i/d_h),
+ *                (k_i, k_{i+d_h/2}) -> (k_i cos a - k_{i+d_h/2} sin a,
+ *                                        k_{i+d_h/2} cos a + k_i sin a),
+ *                t = the key's 0-based position in the cache;
+ *   s_t = q . k^_t / sqrt(d_h), softmax over t < seq_lens[b], out = W_v,g sum p z.
+ * The pages fix neither gamma, eps nor theta, nor the RoPE pairing (these are
+ * the conventions of the Qwen3 models the pages evaluate). q is taken as
+ * already normalised and rotated at its own position.
+ *   k_norm   [d_h]  bf16 (gamma, shared by the kv heads).
+ *   the other arguments, layouts and the workspace as fsq_decode_attn.
+ * Sizes: as fsq_decode_attn, and d_h in {64, 128}, n_q / n_kv <= 32,
+ *        1 < rope_theta < 1e30, 0 <= norm_eps < 1.
+ * Errors: as fsq_decode_attn; FSQ_ERR_NULL (k_norm NULL), FSQ_ERR_SHAPE
+ *         (rope_theta or norm_eps out of range), FSQ_ERR_UNSUPPORTED (d_h).
+ */
+int fsq_decode_attn_rope(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                         const uint16_t *k_norm, const int32_t *seq_lens, uint16_t *out,
+                         int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                         int64_t seq_cap, float rope_theta, float norm_eps, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

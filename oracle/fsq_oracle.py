@@ -18,6 +18,10 @@ What it computes, and where the pages define it (page titles as cited):
   * Query absorption q~_h = W_k,g(h)^T q_h is not on the pages; it is exact for
     the linear key map W_k z used here and is pinned against materialised K/V.
 
+  * Eq. 5 in full, k^_t = RoPE_t(N_k(W_k z_t)) (Architecture, Eq. 5; slides,
+    frame "Attention pools codes before decoding values": keys are rebuilt per
+    position because RoPE depends on it), in decode_attn_rope.
+
 Readings of points the pages leave open:
   * level values are the integers round(u~) in {-8..7}; code = level + 8;
   * rounding is to nearest with ties to even (numpy.rint);
@@ -25,7 +29,13 @@ Readings of points the pages leave open:
     high nibble; for odd G the last high nibble is zero;
   * attention scale 1/sqrt(d_h); q head h reads kv head h // (n_q // n_kv);
   * W_kv rows are [W_k; W_v], each kv-head-major with d_h rows per head;
-  * a sequence of length 0 produces a zero output.
+  * a sequence of length 0 produces a zero output;
+  * Eq. 5's N_k is the model's per-head key RMS norm, k * gamma / sqrt(mean(k^2)
+    + eps), with gamma over the d_h channels shared by the heads; RoPE_t is the
+    rotate-half form on channel pairs (i, i + d_h/2) at angle t * theta^(-2i/d_h),
+    t the 0-based cache position; the pages fix neither gamma, eps nor theta
+    (the tests use gamma from a seed, eps = 1e-6, theta = 1e6); the query is
+    taken as already normalised and rotated at its own position.
 
 Every computation is fp64 on the exact values of the bf16 inputs.
 """
@@ -228,4 +238,55 @@ def decode_partials(q, packed, W_kv, seq_lens, n_kv: int, G: int, bounds):
             l = sum(math.exp(m - M) * li for m, li, _ in parts)
             acc = sum(math.exp(m - M) * a for m, _, a in parts)
             out[b, h] = Wv @ (acc / l)
+    return out
+
+
+# ------------------------------------------------- Eq. 5 keys: N_k and RoPE
+def rms_norm(k, gamma, eps: float) -> np.ndarray:
+    """N_k of Eq. 5 (reading): k * gamma / sqrt(mean(k^2) + eps) over the last
+    axis (the d_h channels of one key head)."""
+    k = np.asarray(k, dtype=np.float64)
+    ms = np.mean(k * k, axis=-1, keepdims=True)
+    return k / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def rope(k, positions, theta: float) -> np.ndarray:
+    """RoPE_t of Eq. 5 (reading: rotate-half pairs). k [..., T, d_h], positions [T].
+    Channel i < d_h/2 and i + d_h/2 form a pair rotated by angle t * theta^(-2i/d_h):
+      out_i        = k_i cos a - k_{i+d_h/2} sin a
+      out_{i+d_h/2} = k_{i+d_h/2} cos a + k_i sin a."""
+    k = np.asarray(k, dtype=np.float64)
+    d_h = k.shape[-1]
+    half = d_h // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / d_h)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]      # [T, half]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = k[..., :half], k[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def decode_attn_rope(q, packed, W_kv, seq_lens, n_kv: int, G: int, gamma, eps: float,
+                     theta: float) -> np.ndarray:
+    """One decode step with the keys of Eq. 5 in full: for each sequence b and
+    query head h (kv head g), over t < seq_lens[b],
+      k^_t = RoPE_t(N_k(W_k,g z_t)),  s_t = q . k^_t / sqrt(d_h),  p = softmax(s),
+      out = W_v,g sum_t p_t z_t       (values still pooled as codes, Eq. 6).
+    Keys are materialised per position (absorption does not apply: N_k is
+    nonlinear and RoPE_t depends on t). Length 0 gives 0. float64 [B, n_q, d_h]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, d_h = q.shape
+    out = np.zeros((B, n_q, d_h), dtype=np.float64)
+    for b in range(B):
+        T = int(seq_lens[b])
+        if T == 0:
+            continue
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G))
+        for g in range(n_kv):
+            Wk, Wv = decoder_blocks(W_kv, g, n_kv, d_h)
+            K = rope(rms_norm(Z @ Wk.T, gamma, eps), np.arange(T), theta)      # [T, d_h]
+            for h in range(g * (n_q // n_kv), (g + 1) * (n_q // n_kv)):
+                s = K @ q[b, h] / math.sqrt(d_h)
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                out[b, h] = Wv @ (Z.T @ p)
     return out

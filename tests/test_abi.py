@@ -152,6 +152,24 @@ def test_decode_recon_validation_before_any_hip_call(args, status):
     assert rc == status
 
 
+@needs_lib
+@pytest.mark.parametrize("args,status", [
+    # (q, codes, W, k_norm, lens, out, batch, n_q, n_kv, d_h, G, cap, theta, eps, ws, ws_bytes)
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 96, 256, 16, 1e6, 1e-6, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 32, 256, 16, 1e6, 1e-6, 256, 1 << 20), fsq.FSQ_ERR_UNSUPPORTED),
+    ((256, 256, 256, 0, 256, 256, 1, 32, 8, 128, 256, 16, 1e6, 1e-6, 256, 1 << 20), fsq.FSQ_ERR_NULL),
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 0.5, 1e-6, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 1e6, -1.0, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, float("nan"), 1e-6, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 0, 32, 8, 128, 256, 16, 1e6, 1e-6, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),
+    ((256, 256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 1e6, 1e-6, 256, 64), fsq.FSQ_ERR_WORKSPACE),
+])
+def test_decode_rope_validation_before_any_hip_call(args, status):
+    (q, c, w, k, l, o, B, nq, nkv, dh, G, cap, th, ep, ws, wsb) = args
+    rc = fsq.lib().fsq_decode_attn_rope(q, c, w, k, l, o, B, nq, nkv, dh, G, cap, th, ep, ws, wsb, None)
+    assert rc == status
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(fsq, "_lib", None)
     monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")

@@ -248,6 +248,42 @@ def test_decode_recon_deterministic(fsq):
     assert np.array_equal(a, run_decode_recon(fsq, q, packed, W, lens, 8))
 
 
+def run_decode_rope(fsq, q_bits, packed, W_bits, gam_bits, lens, n_kv, theta, eps):
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn_rope(q, dev_u8(packed), dev_bf16(W_bits), dev_bf16(gam_bits),
+                             torch.from_numpy(np.asarray(lens, np.int32)).cuda(), out, n_kv, theta, eps)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# Eq. 5 keys in full (key RMS norm with a seeded gain, RoPE at each cache
+# position, theta 1e6 / 1e4, eps 1e-6) against the oracle: positions up to
+# 65536 check the rotation angles far from 0.
+@pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens,theta", [
+    (1, 32, 8, 128, 256, 1024, [1024], 1e6),
+    (2, 32, 8, 128, 84, 1000, [1000, 1], 1e6),
+    (4, 16, 8, 128, 256, 600, [0, 1, 31, 600], 1e4),
+    (1, 8, 1, 64, 37, 130, [129], 1e4),
+    (3, 12, 4, 64, 96, 2100, [2100, 1500, 33], 1e6),
+    (2, 32, 8, 128, 256, 65536, [65536, 4097], 1e6),
+    (4, 32, 8, 128, 84, 65537, [65537, 1, 31, 33], 1e6),
+])
+def test_decode_rope_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens, theta):
+    q, packed, W, lens = decode_case(G * 17 + cap, B, n_q, n_kv, d_h, G, cap, lens)
+    gam = synth.normal_bf16(synth.rng(300, d_h, 0), (d_h,), 0.1)
+    gam = synth.f32_to_bf16_bits(synth.bf16_bits_to_f64(gam).astype(np.float32) + 1.0)
+    got = run_decode_rope(fsq, q, packed, W, gam, lens, n_kv, theta, 1e-6)
+    ref = orc.decode_attn_rope(synth.bf16_bits_to_f64(q), packed, synth.bf16_bits_to_f64(W), lens, n_kv,
+                               G, synth.bf16_bits_to_f64(gam), 1e-6, theta)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            e = rel_l2(got[b], ref[b])
+            assert e < REL_L2, (b, e)
+
+
 def test_decode_deterministic_and_split_invariant(fsq):
     q, packed, W, lens = decode_case(5, 2, 32, 8, 128, 84, 9000, [9000, 4097])
     a = run_decode(fsq, q, packed, W, lens, 8)
