@@ -37,6 +37,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2 ** 20
+COMPARED = ("qwen3_8b_g256", "qwen3_8b_g84")   # workloads of the SDPA and key-reconstruction comparisons
 
 
 def parse():
@@ -45,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_g256", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--also", default="qwen3_8b_g84,qwen3_1p7b_ragged,qwen3_8b_g84_1m",
+    ap.add_argument("--also", default="qwen3_8b_g84,qwen3_1p7b_ragged,qwen3_8b_g84_1m,qwen3_8b_g32,"
+                                      "qwen3_8b_g20,qwen3_8b_l4_g168,qwen3_8b_l256_g42",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true",
@@ -159,6 +161,13 @@ class Model:
         kernel and its inputs are the same)."""
         fsq, w = self.fsq, self.w
         for l, d in enumerate(self.reps[r]):
+            if w.levels != 16:   # 2- / 8-bit codes: append + attention calls
+                for b in range(w.batch):
+                    T = int(self.lens_np[b])
+                    fsq.fsq_append(d["x"][b:b + 1], d["E"], d["codes"][b, T - 1:T], levels=w.levels)
+                fsq.fsq_decode_attn_levels(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv, w.levels,
+                                           workspace=self.ws)
+                continue
             if ev is None and not two_call:
                 fsq.fsq_decode_step(d["x"], d["E"], d["q"], d["codes"], d["W"], self.lens, d["out"],
                                     w.n_kv, workspace=self.ws)
@@ -213,7 +222,7 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
 
     # phase B: eager steps with HIP events around every split-K kernel launch
     call_ms = []
-    for i in range(timing_steps):
+    for i in range(timing_steps if w.levels == 16 else 0):   # the event-timed entry point is 4-bit only
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(w.layers)]
         m.step((warmup + steps + i) % replicas, ev)
@@ -641,17 +650,15 @@ def main():
     sdpa = {}
     if not args.no_sdpa:
         fsq_ms = {w.name: main_res["ms_per_step"], **{k: v["ms_per_step"] for k, v in also.items()}}
-        for name in [args.workload] + [s for s in args.also.split(",") if s]:
+        for name in [n for n in [args.workload] + [s for s in args.also.split(",") if s] if n in COMPARED]:
             r = sdpa_comparison(synth.WORKLOADS[name], torch, fsq_ms[name])
             if r is not None:
                 sdpa[name] = r
     recon = {}
     if not args.no_recon:
         fsq_ms = {w.name: main_res["ms_per_step"], **{k: v["ms_per_step"] for k, v in also.items()}}
-        for name in [args.workload] + [s for s in args.also.split(",") if s]:
+        for name in [n for n in [args.workload] + [s for s in args.also.split(",") if s] if n in COMPARED]:
             w2 = synth.WORKLOADS[name]
-            if w2.ragged or w2.codes_from_fsq:
-                continue
             r = recon_comparison(w2, torch, fsq_ms[name])
             if r is not None:
                 recon[name] = r

@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
-           "fsq_decode_attn_rope")
+           "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_step.restype = ctypes.c_int
         L.fsq_decode_attn_recon.argtypes = L.fsq_decode_attn.argtypes
         L.fsq_decode_attn_recon.restype = ctypes.c_int
+        L.fsq_append_levels.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
+        L.fsq_append_levels.restype = ctypes.c_int
+        L.fsq_decode_attn_levels.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp, sz, vp]
+        L.fsq_decode_attn_levels.restype = ctypes.c_int
         f32 = ctypes.c_float
         L.fsq_decode_attn_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, f32,
                                            vp, sz, vp]
@@ -93,25 +97,36 @@ def _stream(stream) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
-def bytes_per_token(G: int) -> int:
-    return (G + 1) // 2
+LEVEL_BITS = {4: 2, 16: 4, 256: 8}
 
 
-def fsq_append(x: torch.Tensor, E: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
+def bytes_per_token(G: int, levels: int = 16) -> int:
+    return (G * LEVEL_BITS[levels] + 7) // 8
+
+
+def fsq_append(x: torch.Tensor, E: torch.Tensor, codes: torch.Tensor, stream=None,
+               levels: int = 16) -> None:
     """codes[t] = pack(FSQ(E x[t])) for every row of x.
 
-    x [n, C] bf16, E [G, C] bf16, codes [n, ceil(G/2)] uint8 (may be a row range
-    of a cache tensor, e.g. cache[b, T:T+n])."""
+    x [n, C] bf16, E [G, C] bf16, codes [n, ceil(G b/8)] uint8 (may be a row range
+    of a cache tensor, e.g. cache[b, T:T+n]); levels L = 4, 16 (default) or 256."""
     _dev(x, "x", torch.bfloat16, 2)
     _dev(E, "E", torch.bfloat16, 2)
     _dev(codes, "codes", torch.uint8, 2)
     n, C = x.shape
     G = E.shape[0]
+    if levels not in LEVEL_BITS:
+        raise ValueError(f"levels must be one of {sorted(LEVEL_BITS)}")
     if E.shape[1] != C:
         raise ValueError(f"E is {tuple(E.shape)} but x has C={C}")
-    if tuple(codes.shape) != (n, bytes_per_token(G)):
-        raise ValueError(f"codes must be [{n}, {bytes_per_token(G)}], got {tuple(codes.shape)}")
-    rc = lib().fsq_append(x.data_ptr(), E.data_ptr(), codes.data_ptr(), n, C, G, _stream(stream))
+    P = bytes_per_token(G, levels)
+    if tuple(codes.shape) != (n, P):
+        raise ValueError(f"codes must be [{n}, {P}], got {tuple(codes.shape)}")
+    if levels == 16:
+        rc = lib().fsq_append(x.data_ptr(), E.data_ptr(), codes.data_ptr(), n, C, G, _stream(stream))
+    else:
+        rc = lib().fsq_append_levels(x.data_ptr(), E.data_ptr(), codes.data_ptr(), n, C, G, levels,
+                                     _stream(stream))
     _check(rc, "fsq_append")
 
 
@@ -127,7 +142,7 @@ def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv):
+def _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels=16):
     _dev(q, "q", torch.bfloat16, 3)
     _dev(codes, "codes", torch.uint8, 3)
     _dev(W_kv, "W_kv", torch.bfloat16, 2)
@@ -135,8 +150,8 @@ def _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv):
     _dev(out, "out", torch.bfloat16, 3)
     B, n_q, d_h = q.shape
     G = W_kv.shape[1]
-    if codes.shape[0] != B or codes.shape[2] != bytes_per_token(G):
-        raise ValueError(f"codes must be [{B}, cap, {bytes_per_token(G)}], got {tuple(codes.shape)}")
+    if codes.shape[0] != B or codes.shape[2] != bytes_per_token(G, levels):
+        raise ValueError(f"codes must be [{B}, cap, {bytes_per_token(G, levels)}], got {tuple(codes.shape)}")
     if W_kv.shape[0] != 2 * n_kv * d_h:
         raise ValueError(f"W_kv must have {2 * n_kv * d_h} rows, got {W_kv.shape[0]}")
     if seq_lens.shape[0] != B or tuple(out.shape) != (B, n_q, d_h):
@@ -166,6 +181,24 @@ def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes
                                W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q, n_kv,
                                d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(rc, "fsq_decode_step")
+    return out
+
+
+def fsq_decode_attn_levels(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor,
+                           seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int, levels: int,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fsq_decode_attn over a cache of L = levels codes per coordinate (4, 16, 256):
+    codes [B, cap, ceil(G b/8)] uint8, z = code - L/2."""
+    if levels not in LEVEL_BITS:
+        raise ValueError(f"levels must be one of {sorted(LEVEL_BITS)}")
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels)
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, G, cap, q.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    rc = lib().fsq_decode_attn_levels(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(),
+                                      seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, levels,
+                                      cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(rc, "fsq_decode_attn_levels")
     return out
 
 

@@ -6,12 +6,12 @@
 
 namespace fsq {
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
-                         int G, hipStream_t st);
+                         int G, int levels, hipStream_t st);
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                          const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, const uint16_t *x_new,
-                         const uint16_t *E, int C);
+                         const uint16_t *E, int C, int levels);
 hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                                const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out,
                                int batch, int n_q, int n_kv, int d_h, int G, int64_t seq_cap,
@@ -20,6 +20,7 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
 }  // namespace fsq
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+static bool levels_ok(int levels) { return levels == 4 || levels == 16 || levels == 256; }
 
 extern "C" {
 
@@ -35,16 +36,21 @@ const char *fsq_status_string(int status) {
     }
 }
 
-int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_tokens, int32_t C,
-               int32_t G, void *stream) {
+int fsq_append_levels(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_tokens,
+                      int32_t C, int32_t G, int32_t levels, void *stream) {
     if (n_tokens < 0 || C < 1 || G < 1) return FSQ_ERR_SHAPE;
-    if (G > FSQ_MAX_G || C % 8 != 0) return FSQ_ERR_UNSUPPORTED;
+    if (G > FSQ_MAX_G || C % 8 != 0 || !levels_ok(levels)) return FSQ_ERR_UNSUPPORTED;
     if (n_tokens == 0) return FSQ_OK;
     if (!x || !E || !codes) return FSQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(E)) return FSQ_ERR_UNSUPPORTED;
     if (n_tokens > ((int64_t)1 << 31) * 32) return FSQ_ERR_UNSUPPORTED;
-    hipError_t e = fsq::launch_append(x, E, codes, n_tokens, C, G, (hipStream_t)stream);
+    hipError_t e = fsq::launch_append(x, E, codes, n_tokens, C, G, levels, (hipStream_t)stream);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
+}
+
+int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_tokens, int32_t C,
+               int32_t G, void *stream) {
+    return fsq_append_levels(x, E, codes, n_tokens, C, G, 16, stream);
 }
 
 size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap) {
@@ -56,21 +62,24 @@ static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t
                          const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
                          int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
                          size_t workspace_bytes, void *stream, void *ev0, void *ev1,
-                         const uint16_t *x_new = nullptr, const uint16_t *E = nullptr, int32_t C = 0) {
+                         const uint16_t *x_new = nullptr, const uint16_t *E = nullptr, int32_t C = 0,
+                         int32_t levels = 16) {
     if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
-    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH) return FSQ_ERR_UNSUPPORTED;
+    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH || !levels_ok(levels))
+        return FSQ_ERR_UNSUPPORTED;
     if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
     if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
     if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
-    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
-    if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u))
+    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap, levels == 16);
+    if (!workspace || workspace_bytes < fsq::make_decode_plan(batch, n_q, G, seq_cap).total ||
+        ((uintptr_t)workspace & 255u))
         return FSQ_ERR_WORKSPACE;
     // the merge kernel reduces at most 1024 splits (the plan gives <= 512 / batch + 1)
     if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
                                       seq_cap, workspace, (hipStream_t)stream, (hipEvent_t)ev0,
-                                      (hipEvent_t)ev1, x_new, E, C);
+                                      (hipEvent_t)ev1, x_new, E, C, levels);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
 }
 
@@ -80,6 +89,15 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
                     size_t workspace_bytes, void *stream) {
     return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
                          workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int fsq_decode_attn_levels(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                           const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                           int32_t n_kv, int32_t d_h, int32_t G, int32_t levels, int64_t seq_cap,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                         workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr, 0,
+                         levels);
 }
 
 int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,

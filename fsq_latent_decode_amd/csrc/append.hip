@@ -1,6 +1,8 @@
-// Append path: u = E x (Eq. 4), the Eq. 2 bound and round in fp32, and 4-bit
-// packing (slides "Transformer-FSQ", frame "A wide product code uses four bits
-// per coordinate": ceil(G b / 8) bytes per token, no metadata).
+// Append path: u = E x (Eq. 4), the Eq. 2 bound and round in fp32, and packing
+// at b = 4 bits per code (slides "Transformer-FSQ", frame "A wide product code
+// uses four bits per coordinate": ceil(G b / 8) bytes per token, no metadata),
+// or 2 / 8 bits for L = 4 / 256 levels (backup frame "the grid size is an
+// allocation choice").
 //
 // Two kernels, chosen by the number of tokens:
 //   append_mfma_kernel  n >= 32: one CTA per 32 tokens, bf16 MFMA 32x32x16 with
@@ -16,11 +18,11 @@ namespace fsq {
 
 constexpr int kAppendWaves = 4;
 
-template <int NT>
+template <int NT, int CPB>
 __global__ __launch_bounds__(kGemvWaves * 64) void append_gemv_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ E, uint8_t *__restrict__ codes, int n,
-    int C, int G, float shift) {
-    append_gemv_body<NT>(blockIdx.x, blockIdx.y * NT, x, E, codes, n, C, G, shift, nullptr, 0);
+    int C, int G, FsqQuant fq) {
+    append_gemv_body<NT, CPB>(blockIdx.x, blockIdx.y * NT, x, E, codes, n, C, G, fq, nullptr, 0);
 }
 
 // Prefill path. A CTA of 4 waves computes u = E x for 32 tokens; the waves
@@ -61,7 +63,7 @@ __device__ inline int append_swz(int row) {
 template <int GP>
 __global__ __launch_bounds__(kAppendWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void append_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ E, uint8_t *__restrict__ codes,
-    int64_t n, int C, int G, float shift) {
+    int64_t n, int C, int G, FsqQuant fq, int bits) {
     using A = AppendCfg<GP>;
     constexpr int CB = A::CB, KPB = A::KPB, RL = A::RL, CPR = A::CPR, RPI = A::RPI;
     constexpr int XI = A::XI, EI = A::EI, KS = A::KS, NB = A::NB, SLOT = A::SLOT;
@@ -161,46 +163,62 @@ __global__ __launch_bounds__(kAppendWaves * 64) __attribute__((amdgpu_waves_per_
         }
         __syncthreads();
     }
-    // FSQ + pack: one thread per output byte
-    const int P = bytes_per_token(G);
+    // FSQ + pack: one thread per output byte (8 / bits codes, little-endian)
+    const int cpb = 8 / bits;
+    const int P = bytes_per_token_b(G, bits);
     uint8_t *dst = codes + (size_t)tile0 * P;
     for (int idx = threadIdx.x; idx < rows * P; idx += blockDim.x) {
         const int tok = idx / P, j = idx - tok * P;
-        const uint32_t q0 = fsq_code(U[tok * ROW + 2 * j], shift);
-        const uint32_t q1 = (2 * j + 1 < G) ? fsq_code(U[tok * ROW + 2 * j + 1], shift) : 0u;
-        dst[idx] = (uint8_t)(q0 | (q1 << 4));
+        uint32_t byte = 0;
+        for (int c = 0; c < cpb; ++c) {
+            const int k = cpb * j + c;
+            if (k < G) byte |= fsq_code(U[tok * ROW + k], fq) << (bits * c);
+        }
+        dst[idx] = (uint8_t)byte;
     }
 }
 
 template <int GP>
 static hipError_t launch_append_mfma(const uint16_t *x, const uint16_t *E, uint8_t *codes,
-                                     int64_t n, int C, int G, float shift, hipStream_t st) {
+                                     int64_t n, int C, int G, const FsqQuant &fq, int bits,
+                                     hipStream_t st) {
     const int64_t tiles = (n + 31) / 32;
     append_mfma_kernel<GP><<<dim3((unsigned)tiles), kAppendWaves * 64, 0, st>>>(x, E, codes, n, C, G,
-                                                                               shift);
+                                                                               fq, bits);
     return hipGetLastError();
 }
 
+template <int CPB>
+static void launch_append_gemv(const uint16_t *x, const uint16_t *E, uint8_t *codes, int n, int C,
+                               int G, const FsqQuant &fq, hipStream_t st) {
+    const int nt = gemv_tokens_per_cta(n);
+    dim3 grid(bytes_per_token_b(G, 8 / CPB), (unsigned)((n + nt - 1) / nt));
+    switch (nt) {
+        case 1: append_gemv_kernel<1, CPB><<<grid, 256, 0, st>>>(x, E, codes, n, C, G, fq); break;
+        case 2: append_gemv_kernel<2, CPB><<<grid, 256, 0, st>>>(x, E, codes, n, C, G, fq); break;
+        case 4: append_gemv_kernel<4, CPB><<<grid, 256, 0, st>>>(x, E, codes, n, C, G, fq); break;
+        default: append_gemv_kernel<kGemvTokens, CPB><<<grid, 256, 0, st>>>(x, E, codes, n, C, G, fq);
+    }
+}
+
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
-                         int G, hipStream_t st) {
-    const float shift = host_fsq_shift();
+                         int G, int levels, hipStream_t st) {
+    const FsqQuant fq = host_fsq_quant(levels);
+    const int bits = bits_of_levels(levels);
     if (n < 32) {
-        const int nt = gemv_tokens_per_cta(n);
-        dim3 grid(bytes_per_token(G), (unsigned)((n + nt - 1) / nt));
-        switch (nt) {
-            case 1: append_gemv_kernel<1><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
-            case 2: append_gemv_kernel<2><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
-            case 4: append_gemv_kernel<4><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift); break;
-            default:
-                append_gemv_kernel<kGemvTokens><<<grid, 256, 0, st>>>(x, E, codes, (int)n, C, G, shift);
-        }
+        if (bits == 2)
+            launch_append_gemv<4>(x, E, codes, (int)n, C, G, fq, st);
+        else if (bits == 8)
+            launch_append_gemv<1>(x, E, codes, (int)n, C, G, fq, st);
+        else
+            launch_append_gemv<2>(x, E, codes, (int)n, C, G, fq, st);
         return hipGetLastError();
     }
     const int GP = (G + 31) / 32 * 32;
     switch (GP) {
 #define FSQ_APPEND_CASE(X) \
     case X:                \
-        return launch_append_mfma<X>(x, E, codes, n, C, G, shift, st);
+        return launch_append_mfma<X>(x, E, codes, n, C, G, fq, bits, st);
         FSQ_APPEND_CASE(32)
         FSQ_APPEND_CASE(64)
         FSQ_APPEND_CASE(96)

@@ -1,5 +1,5 @@
-// Append of a few tokens (u = E x, Eq. 4; the Eq. 2 bound and round; 4-bit
-// packing) as a device-side body shared by the append kernel and the fused
+// Append of a few tokens (u = E x, Eq. 4; the Eq. 2 bound and round; packing
+// at 2, 4 or 8 bits per code) as a device-side body shared by the append kernel and the fused
 // decode-step kernel, so both produce bit-identical codes.
 #pragma once
 
@@ -20,37 +20,45 @@ __device__ inline float dot8_bf16(u32x4 a, u32x4 b) {
     return s;
 }
 
-// Output byte j (coordinates 2j, 2j+1) of tokens tb .. tb + NT - 1 (< n).
+// Output byte j of tokens tb .. tb + NT - 1 (< n): the CPB = 8 / bits codes of
+// coordinates CPB j .. CPB j + CPB - 1 (past G: zero bits), code i of the byte
+// at bits i * bits (little-endian within the byte).
 // Destination row of token i: row i of a dense [n, P] array when lens is null;
 // otherwise row lens[i] - 1 of sequence i in a [n, seq_cap, P] cache, skipped
 // unless 1 <= lens[i] <= seq_cap. The per-token arithmetic does not depend on NT.
-template <int NT>
+template <int NT, int CPB>
 __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, int tb, const uint16_t *__restrict__ x,
                                         const uint16_t *__restrict__ E, uint8_t *__restrict__ codes,
-                                        int n, int C, int G, float shift,
+                                        int n, int C, int G, const FsqQuant &fq,
                                         const int32_t *__restrict__ lens, int64_t seq_cap) {
-    __shared__ float red[kGemvWaves][NT][2];
+    constexpr int BITS = 8 / CPB;
+    __shared__ float red[kGemvWaves][NT][CPB];
     const int nt = (n - tb) < NT ? (n - tb) : NT;
-    const int c0 = 2 * j, c1 = 2 * j + 1;
-    const bool has1 = c1 < G;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float acc[NT][2];
+    float acc[NT][CPB];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = 0.0f;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) acc[t][c] = 0.0f;
     const int nv = C / 8;
-    const u32x4 *e0p = reinterpret_cast<const u32x4 *>(E + (size_t)c0 * C);
-    const u32x4 *e1p = reinterpret_cast<const u32x4 *>(E + (size_t)(has1 ? c1 : c0) * C);
+    const u32x4 *ep[CPB];
+    bool has[CPB];
+#pragma unroll
+    for (int c = 0; c < CPB; ++c) {
+        has[c] = CPB * j + c < G;
+        ep[c] = reinterpret_cast<const u32x4 *>(E + (size_t)(has[c] ? CPB * j + c : CPB * j) * C);
+    }
     // two vectors per thread and pass, all loads issued before the first use
     // (clamped indices); each thread accumulates its vectors in index order
     constexpr int U = 2;
     const int nthr = kGemvWaves * 64;
     for (int v0 = threadIdx.x; v0 < nv; v0 += U * nthr) {
-        u32x4 e0[U], e1[U], xv[U][NT];
+        u32x4 ev[U][CPB], xv[U][NT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * nthr < nv ? v0 + u * nthr : nv - 1;
-            e0[u] = e0p[v];
-            e1[u] = has1 ? e1p[v] : u32x4{};
+#pragma unroll
+            for (int c = 0; c < CPB; ++c) ev[u][c] = has[c] ? ep[c][v] : u32x4{};
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 if (t < nt) xv[u][t] = reinterpret_cast<const u32x4 *>(x + (size_t)(tb + t) * C)[v];
@@ -61,8 +69,8 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     if (t < nt) {
-                        acc[t][0] += dot8_bf16(e0[u], xv[u][t]);
-                        acc[t][1] += dot8_bf16(e1[u], xv[u][t]);
+#pragma unroll
+                        for (int c = 0; c < CPB; ++c) acc[t][c] += dot8_bf16(ev[u][c], xv[u][t]);
                     }
                 }
             }
@@ -71,7 +79,7 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < CPB; ++c) {
             float a = acc[t][c];
             for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off);
             if (lane == 0) red[wave][t][c] = a;
@@ -79,14 +87,14 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
     __syncthreads();
     if (threadIdx.x < nt) {
         const int t = threadIdx.x;
-        float u0 = 0.0f, u1 = 0.0f;
-        for (int w = 0; w < kGemvWaves; ++w) {
-            u0 += red[w][t][0];
-            u1 += red[w][t][1];
+        uint32_t byte = 0;
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) {
+            float u = 0.0f;
+            for (int w = 0; w < kGemvWaves; ++w) u += red[w][t][c];
+            if (has[c]) byte |= fsq_code(u, fq) << (BITS * c);
         }
-        const uint32_t q0 = fsq_code(u0, shift);
-        const uint32_t q1 = has1 ? fsq_code(u1, shift) : 0u;
-        const int P = bytes_per_token(G);
+        const int P = bytes_per_token_b(G, BITS);
         size_t row;
         if (lens == nullptr) {
             row = (size_t)(tb + t);
@@ -95,7 +103,7 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
             if (len < 1 || len > seq_cap) return;
             row = (size_t)(tb + t) * (size_t)seq_cap + (size_t)(len - 1);
         }
-        codes[row * P + j] = (uint8_t)(q0 | (q1 << 4));
+        codes[row * P + j] = (uint8_t)byte;
     }
 }
 

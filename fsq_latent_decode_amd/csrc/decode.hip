@@ -45,6 +45,20 @@ __device__ inline half8 unpack_codes(uint32_t w) {
     const u32x4 t = {w & m, (w >> 4) & m, (w >> 8) & m, (w >> 12) & m};
     return __builtin_bit_cast(half8, t);
 }
+// 8-bit codes (L = 256): two packed dwords, 4 codes each, as fp16 subnormals
+// n * 2^-24 in the order (c0,c2) (c1,c3) (c4,c6) (c5,c7).
+__device__ inline half8 unpack_codes8(uint32_t w0, uint32_t w1) {
+    const uint32_t m = 0x00FF00FFu;
+    const u32x4 t = {w0 & m, (w0 >> 8) & m, w1 & m, (w1 >> 8) & m};
+    return __builtin_bit_cast(half8, t);
+}
+// 2-bit codes (L = 4): half of a packed dword of 16 codes (upper = 0: codes
+// 0..3 and 8..11, upper = 1: 4..7 and 12..15) in the order (c_i, c_i+8).
+__device__ inline half8 unpack_codes2(uint32_t w, int upper) {
+    const uint32_t m = 0x00030003u, v = upper ? w >> 8 : w;
+    const u32x4 t = {v & m, (v >> 2) & m, (v >> 4) & m, (v >> 6) & m};
+    return __builtin_bit_cast(half8, t);
+}
 
 // ---------------------------------------------------------------- absorb
 // q~[b, h, pos(k)] = scale * sum_d W_k[g d_h + d, k] q[b, h, d] for the heads h
@@ -85,7 +99,7 @@ template <int VW>
 __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
                                    int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
-                                   float odd_scale) {
+                                   float odd_scale, int bits) {
     using A = AbsorbCfg<VW>;
     using VT = typename VecT<VW>::T;
     __shared__ float qs[kAbsorbHeads][kMaxDh];
@@ -161,7 +175,7 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
                 for (int r = 0; r < A::DG; ++r) sum += red[r][j][col];
                 const int h = g * grp + hb + j;
                 const float sk = (k & 1) ? scale * odd_scale : scale;
-                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP)] = (_Float16)(k < G ? sum * sk : 0.0f);
+                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP, bits)] = (_Float16)(k < G ? sum * sk : 0.0f);
             }
         }
         __syncthreads();
@@ -175,12 +189,12 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ W_kv,
                                                      _Float16 *__restrict__ qt, int G, int GP,
                                                      int n_q, int nqp, int n_kv, int d_h, float scale,
-                                                     float odd_scale) {
+                                                     float odd_scale, int bits) {
     const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
     int r = blockIdx.x;
     const int g = r % n_kv;
     r /= n_kv;
-    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale);
+    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
 }
 
 // ---------------------------------------------------------- decode step
@@ -193,7 +207,7 @@ struct StepAppend {
     const uint16_t *x_new, *E;
     uint8_t *codes;
     int C;
-    float shift;
+    FsqQuant fq;   // L = 16
 };
 
 template <int NT, int VW>
@@ -207,14 +221,14 @@ __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int
     const int bx = blockIdx.x;
     const int P = bytes_per_token(G);
     if (bx < n_app) {
-        append_gemv_body<NT>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.shift,
+        append_gemv_body<NT, 2>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.fq,
                              seq_lens, seq_cap);
     } else {
         const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
         int r = bx - n_app;
         const int g = r % n_kv;
         r /= n_kv;
-        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale);
+        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, 4);
     }
 }
 
@@ -259,14 +273,17 @@ struct SplitCfg {
 // both fall on distinct LDS banks.
 __device__ inline int zt_swz(int row) { return 16 * (row & 3) + 4 * ((row >> 2) & 3); }
 
-template <int GP, int NW, bool AL>
+template <int GP, int NW, bool AL, int BITS>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
     float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S) {
     using C = SplitCfg<GP, NW>;
     constexpr int KB = C::KB, CB = C::CB, CBW = C::CBW, RS = C::RS;
-    constexpr int NLD = AL ? KB : KB + 1;   // dwords loaded per lane per tile
+    constexpr int HB = GP * BITS / 16;       // bytes of a lane's half of a token row
+    constexpr int ND = HB / 4;               // packed dwords per half (KB operands of 8 codes)
+    constexpr int NLD = AL ? ND : ND + 1;   // dwords loaded per lane per tile
+    static_assert(!AL || ND % 2 == 0, "8-byte loads of whole halves");
     // the reference max may lag the true max by this much (log2 units) before the
     // accumulators are rescaled: p = 2^(s - m) stays <= 256, exact range for fp16
     constexpr float kRescaleSlack = 8.0f;
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t psm[C::kPBytes];
     __shared__ float tmax_s[NW][32], tsum_s[NW][32];
 
-    const int P = (G + 1) / 2;
+    const int P = bytes_per_token_b(G, BITS);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
     const int64_t c0 = (int64_t)s * chunk;   // < seq_cap: the grid has ceil(seq_cap / chunk) chunks
@@ -294,17 +311,17 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         if (ld_ntok == 0) return;
         const int tc = t < ld_ntok ? t : ld_ntok - 1;
         if (AL) {
-            // P == GP / 2 and P % 16 == 0: the half is KB whole, 8-byte aligned dwords
-            const uint2 *src = reinterpret_cast<const uint2 *>(seq + (size_t)(t0 + tc) * P + hh * (GP / 4));
+            // G == GP and P % 16 == 0: the half is ND whole, 8-byte aligned dwords
+            const uint2 *src = reinterpret_cast<const uint2 *>(seq + (size_t)(t0 + tc) * P + hh * HB);
 #pragma unroll
-            for (int i = 0; i < KB / 2; ++i) {
+            for (int i = 0; i < ND / 2; ++i) {
                 const uint2 v = src[i];
                 ld[2 * i] = v.x;
                 ld[2 * i + 1] = v.y;
             }
         } else {
             // aligned dwords around the half, clamped to the tile's last dword
-            const uint8_t *a = seq + (size_t)(t0 + tc) * P + hh * (GP / 4);
+            const uint8_t *a = seq + (size_t)(t0 + tc) * P + hh * HB;
             ld_sh = (int)((uintptr_t)a & 3) * 8;
             const uint32_t *a0 = reinterpret_cast<const uint32_t *>(a - ((uintptr_t)a & 3));
             const uint8_t *lastb = seq + (size_t)(t0 + ld_ntok) * P - 1;
@@ -368,15 +385,15 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 
     for (int64_t r0 = c0; r0 < c1; r0 += NW * kTile) {
         // ---- phase 1: own tile -> fp16 codes -> LDS tile + scores
-        uint32_t cur[KB];
+        uint32_t cur[ND];
         const int ntok = ld_ntok;
         const int sh = ld_sh;
         if (AL) {
 #pragma unroll
-            for (int i = 0; i < KB; ++i) cur[i] = ld[i];
+            for (int i = 0; i < ND; ++i) cur[i] = ld[i];
         } else {
 #pragma unroll
-            for (int i = 0; i < KB; ++i)
+            for (int i = 0; i < ND; ++i)
                 cur[i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
         }
         issue(r0 + NW * kTile + wave * kTile);
@@ -390,7 +407,9 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         floatx16 sc = floatx16{};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const half8 z = unpack_codes(cur[kb]);
+            const half8 z = BITS == 8   ? unpack_codes8(cur[2 * kb], cur[2 * kb + 1])
+                            : BITS == 2 ? unpack_codes2(cur[kb >> 1], kb & 1)
+                                        : unpack_codes(cur[kb]);
             *reinterpret_cast<half8 *>(zt_own + t * RS + ((8 * kb + 4 * hh) ^ zt_swz(t))) = z;
             sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc, 0, 0, 0);
         }
@@ -490,7 +509,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 
     // ---- epilogue: zbar = acc / l in operand-position order, fp16, stored from
     // registers: each lane holds head t and, per block, 4 runs of 4 positions
-    const float zscale = kCodeScale / l_run;   // codes n * 2^-24 pooled: zbar = 2^24 acc / l - 8
+    const float zscale = kCodeScale / l_run;   // codes n * 2^-24 pooled: zbar = 2^24 acc / l - L/2
+    constexpr float kLevelOffset = (float)(1 << (BITS - 1));
     const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
     const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -503,10 +523,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             if (CB % NW == 0 || cb < CB) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const half4 v = {(_Float16)fmaf(acc[j][4 * r4 + 0], zscale, -8.0f),
-                                     (_Float16)fmaf(acc[j][4 * r4 + 1], zscale, -8.0f),
-                                     (_Float16)fmaf(acc[j][4 * r4 + 2], zscale, -8.0f),
-                                     (_Float16)fmaf(acc[j][4 * r4 + 3], zscale, -8.0f)};
+                    const half4 v = {(_Float16)fmaf(acc[j][4 * r4 + 0], zscale, -kLevelOffset),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 1], zscale, -kLevelOffset),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 2], zscale, -kLevelOffset),
+                                     (_Float16)fmaf(acc[j][4 * r4 + 3], zscale, -kLevelOffset)};
                     *reinterpret_cast<half4 *>(dst + cb * 32 + r4 * 8 + hh * 4) = v;
                 }
             }
@@ -1099,7 +1119,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
-    int chunk, int S, int natural) {
+    int chunk, int S, int natural, int bits) {
     using VT = typename VecT<VW>::T;
     // W_v vectors per thread held in registers (two or more threads per row);
     // narrow vectors (odd G) beyond 32 per thread are read in the dot loop
@@ -1218,7 +1238,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     for (int p = tid; p < GP; p += blockDim.x) {
         float z = 0.0f;
         for (int u = 0; u < SG; ++u) z += zpart[u * GP + p];
-        zbar[natural ? p : pos_to_coord(p, GP)] = z * invL;
+        zbar[natural ? p : pos_to_coord(p, GP, bits)] = z * invL;
     }
     __syncthreads();
 
@@ -1255,7 +1275,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     }
 }
 
-template <int GP, int NW>
+template <int GP, int NW, int BITS>
 static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
                                   const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                   int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
@@ -1263,8 +1283,10 @@ static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, cons
     dim3 grid(pl.S, batch, pl.nqp / 32);
     dim3 block(NW * 64);
     // whole-dword vector loads when every token row starts on a 16-byte boundary
-    const bool al = G == GP && ((G / 2) % 16) == 0 && ((uintptr_t)codes & 15) == 0;
-    auto k = al ? decode_split_kernel<GP, NW, true> : decode_split_kernel<GP, NW, false>;
+    constexpr bool kCanAl = (GP * BITS / 64) % 2 == 0;
+    const bool al = kCanAl && G == GP && (bytes_per_token_b(G, BITS) % 16) == 0 &&
+                    ((uintptr_t)codes & 15) == 0;
+    auto k = al ? decode_split_kernel<GP, NW, kCanAl, BITS> : decode_split_kernel<GP, NW, false, BITS>;
     if (ev0 && ev1)   // timed launch: events bracket this kernel's execution
         hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
                               seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S);
@@ -1319,7 +1341,15 @@ template <int GP>
 static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const uint8_t *codes,
                                const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
-                               hipEvent_t ev1) {
+                               hipEvent_t ev1, int bits) {
+    if (bits != 4) {   // 2- and 8-bit codes: the split kernel only
+        if (pl.stream || pl.waves != split_waves(GP)) return hipErrorInvalidValue;
+        constexpr int NW = GP >= 128 ? 8 : 4;
+        return bits == 2 ? launch_split_nw<GP, NW, 2>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                      batch, st, ev0, ev1)
+                         : launch_split_nw<GP, NW, 8>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                      batch, st, ev0, ev1);
+    }
     if (pl.stream) {
         if (pl.waves != kStreamWaves) return hipErrorInvalidValue;
         constexpr int D = GP >= 128 ? 3 : 4;   // stream_depth(GP)
@@ -1328,15 +1358,16 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
                                       ev0, ev1);
     }
     if (pl.waves != split_waves(GP)) return hipErrorInvalidValue;
-    return launch_split_nw<GP, (GP >= 128 ? 8 : 4)>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
-                                                    batch, st, ev0, ev1);
+    return launch_split_nw<GP, (GP >= 128 ? 8 : 4), 4>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                       batch, st, ev0, ev1);
 }
 
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,
                          const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int batch,
                          int n_q, int n_kv, int d_h, int G, int64_t seq_cap, void *workspace,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, const uint16_t *x_new,
-                         const uint16_t *E, int C) {
+                         const uint16_t *E, int C, int levels) {
+    const int bits = bits_of_levels(levels);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *qt = reinterpret_cast<_Float16 *>(ws + pl.off_qt);
     _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
@@ -1352,7 +1383,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
                                                                    : 1;
     if (pl.S > 0 && x_new) {
         // decode step: append + absorb in one launch
-        const StepAppend ap{x_new, E, const_cast<uint8_t *>(codes), C, host_fsq_shift()};
+        const StepAppend ap{x_new, E, const_cast<uint8_t *>(codes), C, host_fsq_quant(16)};
         const int nt = gemv_tokens_per_cta(batch);
         const int n_app = bytes_per_token(G) * ((batch + nt - 1) / nt);
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
@@ -1371,10 +1402,10 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
         const dim3 ag((unsigned)n_abs);
         switch (vw) {
-            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
-            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
-            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd); break;
-            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd);
+            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
+            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
+            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
+            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1382,7 +1413,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         switch (pl.GP) {
 #define FSQ_SPLIT_CASE(X)                                                                             \
     case X:                                                                                           \
-        e = launch_split<X>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1); \
+        e = launch_split<X>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1, bits); \
         break;
             FSQ_SPLIT_CASE(32)
             FSQ_SPLIT_CASE(64)
@@ -1399,7 +1430,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         if (e != hipSuccess) return e;
     }
     const dim3 mg(n_q, batch);
-#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S, pl.stream
+#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S, pl.stream, bits
     switch (vw) {
         case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
         case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
@@ -1472,7 +1503,7 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
                                                                    : 1;
     const dim3 mg(n_q, batch);
     const int chunk_i = S > 0 ? (int)chunk : pl.chunk;
-#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, chunk_i, (S > 0 ? S : 1), 1
+#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, chunk_i, (S > 0 ? S : 1), 1, 4
     switch (vw) {
         case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
         case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;

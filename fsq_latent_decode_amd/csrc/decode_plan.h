@@ -39,7 +39,9 @@ struct DecodePlan {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
+// allow_stream = false (codes of 2 or 8 bits) keeps the split kernel; its split
+// count never exceeds the default plan's, so the default workspace suffices.
+inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, bool allow_stream = true) {
     DecodePlan p;
     p.GP = (G + 31) / 32 * 32;
     p.nqp = (n_q + 31) / 32 * 32;
@@ -48,7 +50,7 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap) {
     const int starget = stream_target(p.GP);
     int64_t sper = (work + starget - 1) / starget;
     sper = (sper + squant - 1) / squant * squant;
-    p.stream = sper >= (int64_t)kStreamMinTiles * squant ? 1 : 0;
+    p.stream = allow_stream && sper >= (int64_t)kStreamMinTiles * squant ? 1 : 0;
     p.waves = p.stream ? kStreamWaves : split_waves(p.GP);
     const int quantum = 32 * p.waves;
     const int target = p.stream ? starget : (p.waves == 8 ? 256 : 512);

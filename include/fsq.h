@@ -31,6 +31,12 @@
  *   byte j of a token = code[2j] | (code[2j+1] << 4), j < ceil(G/2); for odd G
  *   the last high nibble is zero. A token row is exactly ceil(G/2) bytes; rows
  *   of one sequence are contiguous.
+ * The *_levels entry points take L = 4, 16 or 256 levels (b = 2, 4, 8 bits per
+ * code; the slides' backup frame "the grid size is an allocation choice"):
+ * h = 1.001 (L - 1) / 2 (a reading: the pages print h only for L = 16, where
+ * this gives 7.5075), delta = 0.5, levels -L/2 .. L/2 - 1, code = level + L/2,
+ * code i of a token at bits (i b) mod 8 of byte floor(i b / 8), unused high
+ * bits of the last byte zero; a row is ceil(G b / 8) bytes.
  */
 #ifndef FSQ_H
 #define FSQ_H
@@ -83,6 +89,15 @@ int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes,
                int64_t n_tokens, int32_t C, int32_t G, void *stream);
 
 /*
+ * fsq_append_levels - fsq_append for L = levels per coordinate (4, 16 or 256;
+ * the layout above); codes rows are ceil(G b / 8) bytes. fsq_append is
+ * fsq_append_levels with levels = 16.
+ * Errors: as fsq_append; FSQ_ERR_UNSUPPORTED for another number of levels.
+ */
+int fsq_append_levels(const uint16_t *x, const uint16_t *E, uint8_t *codes,
+                      int64_t n_tokens, int32_t C, int32_t G, int32_t levels, void *stream);
+
+/*
  * fsq_decode_workspace_bytes - device workspace that fsq_decode_attn needs for
  * these sizes (the absorbed queries and the split-K partial states).
  * Returns 0 for invalid sizes. Depends only on its arguments.
@@ -127,6 +142,19 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
                     int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
                     int64_t seq_cap, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * fsq_decode_attn_levels - fsq_decode_attn over a cache of L = levels codes
+ * per coordinate (4, 16 or 256; rows of ceil(G b / 8) bytes, the layout
+ * above), z_t = code_t - L/2. Same workspace size as fsq_decode_attn for the
+ * same sizes. fsq_decode_attn is this call with levels = 16.
+ * Errors: as fsq_decode_attn; FSQ_ERR_UNSUPPORTED for another number of levels.
+ */
+int fsq_decode_attn_levels(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                           const int32_t *seq_lens, uint16_t *out,
+                           int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                           int32_t levels, int64_t seq_cap, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * fsq_decode_attn_timed - fsq_decode_attn that also records two caller-created

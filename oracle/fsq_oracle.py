@@ -61,23 +61,33 @@ def fsq_bound(u, h: float = H_BOUND, delta: float = DELTA) -> np.ndarray:
     return h * np.tanh(u + math.atanh(delta / h)) - delta
 
 
-def fsq_levels(u) -> np.ndarray:
+def h_of_levels(levels: int) -> float:
+    """Bound h of Eq. 2 for L levels. The pages print h only for L = 16 (7.5075,
+    slides footnote); reading for L = 4 and 256 (the slides' backup frame "the
+    grid size is an allocation choice"): h = 1.001 (L - 1) / 2, which gives
+    7.5075 at L = 16, with delta = 0.5 and levels -L/2 .. L/2 - 1."""
+    return 1.001 * (levels - 1) / 2.0
+
+
+def fsq_levels(u, levels: int = LEVELS) -> np.ndarray:
     """Forward value of Eq. 2: the rounded bounded coordinate round(u~).
 
     The straight-through term sg(round(u~) - u~) only changes gradients; in the
-    forward pass u^ equals round(u~) exactly. Result is an int64 level in -8..7."""
-    lv = np.rint(fsq_bound(u))
-    if lv.size and (lv.min() < -CODE_OFFSET or lv.max() > CODE_OFFSET - 1):
-        raise AssertionError("FSQ level outside -8..7")
+    forward pass u^ equals round(u~) exactly. Result is an int64 level in
+    -L/2 .. L/2 - 1 (-8..7 for L = 16)."""
+    h = H_BOUND if levels == LEVELS else h_of_levels(levels)
+    lv = np.rint(fsq_bound(u, h=h))
+    if lv.size and (lv.min() < -(levels // 2) or lv.max() > levels // 2 - 1):
+        raise AssertionError("FSQ level outside the grid")
     return lv.astype(np.int64)
 
 
-def fsq_codes(u) -> np.ndarray:
-    """Code of each coordinate: level + 8, a value in 0..15 (uint8)."""
-    return (fsq_levels(u) + CODE_OFFSET).astype(np.uint8)
+def fsq_codes(u, levels: int = LEVELS) -> np.ndarray:
+    """Code of each coordinate: level + L/2, a value in 0..L-1 (uint8)."""
+    return (fsq_levels(u, levels) + levels // 2).astype(np.uint8)
 
 
-def encode(x, E) -> np.ndarray:
+def encode(x, E, levels: int = LEVELS) -> np.ndarray:
     """Eq. 4: z_t = Q_FSQ(E x_t) for every row x_t of x.
 
     x [N, C] and E [G, C] as float64 (the exact bf16 values). Returns codes
@@ -85,7 +95,7 @@ def encode(x, E) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     E = np.asarray(E, dtype=np.float64)
     u = x @ E.T
-    return fsq_codes(u)
+    return fsq_codes(u, levels)
 
 
 def projection(x, E) -> np.ndarray:
@@ -106,37 +116,47 @@ def full_cache_bytes(n_kv: int, d_h: int, elem_bytes: int = 2) -> int:
     return 2 * n_kv * d_h * elem_bytes
 
 
-def pack_codes(codes) -> np.ndarray:
-    """[N, G] codes in 0..15 -> [N, ceil(G/2)] bytes; byte j = c[2j] | c[2j+1] << 4."""
+def pack_codes(codes, bits: int = BITS) -> np.ndarray:
+    """[N, G] codes of b bits -> [N, ceil(G b/8)] bytes; byte j holds codes
+    c[k j + i], i < k = 8 / b, at bits b i (4 bits: c[2j] | c[2j+1] << 4)."""
     codes = np.asarray(codes, dtype=np.uint8)
     N, G = codes.shape
-    if codes.size and codes.max() > 15:
-        raise AssertionError("code outside 0..15")
-    P = bytes_per_token(G)
-    padded = np.zeros((N, 2 * P), dtype=np.uint8)
+    if codes.size and int(codes.max()) >= (1 << bits):
+        raise AssertionError("code outside the b-bit range")
+    k = 8 // bits
+    P = bytes_per_token(G, bits)
+    padded = np.zeros((N, k * P), dtype=np.uint8)
     padded[:, :G] = codes
     out = np.zeros((N, P), dtype=np.uint8)
     for j in range(P):
-        out[:, j] = padded[:, 2 * j] | (padded[:, 2 * j + 1] << 4)
+        for i in range(k):
+            out[:, j] |= (padded[:, k * j + i] << (bits * i)).astype(np.uint8)
     return out
 
 
-def unpack_codes(packed, G: int) -> np.ndarray:
-    """Inverse of pack_codes: [N, ceil(G/2)] bytes -> [N, G] codes."""
+def unpack_codes(packed, G: int, bits: int = BITS) -> np.ndarray:
+    """Inverse of pack_codes: [N, ceil(G b/8)] bytes -> [N, G] codes."""
     packed = np.asarray(packed, dtype=np.uint8)
     N, P = packed.shape
-    if P != bytes_per_token(G):
+    if P != bytes_per_token(G, bits):
         raise ValueError("packed width does not match G")
-    out = np.zeros((N, 2 * P), dtype=np.uint8)
+    k = 8 // bits
+    mask = (1 << bits) - 1
+    out = np.zeros((N, k * P), dtype=np.uint8)
     for j in range(P):
-        out[:, 2 * j] = packed[:, j] & 0x0F
-        out[:, 2 * j + 1] = packed[:, j] >> 4
+        for i in range(k):
+            out[:, k * j + i] = (packed[:, j] >> (bits * i)) & mask
     return out[:, :G]
 
 
-def levels_of_codes(codes) -> np.ndarray:
-    """Latent values z = code - 8 as float64 (the grid points of Eq. 3)."""
-    return np.asarray(codes, dtype=np.float64) - CODE_OFFSET
+def levels_of_codes(codes, levels: int = LEVELS) -> np.ndarray:
+    """Latent values z = code - L/2 as float64 (the grid points of Eq. 3)."""
+    return np.asarray(codes, dtype=np.float64) - levels // 2
+
+
+def bits_of_levels(levels: int) -> int:
+    """b = log2 L for L = 4, 16, 256."""
+    return {4: 2, 16: 4, 256: 8}[levels]
 
 
 # ------------------------------------------------------- latent-space decode
@@ -153,7 +173,7 @@ def decoder_blocks(W_kv, g: int, n_kv: int, d_h: int):
     return Wk, Wv
 
 
-def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
+def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int, levels: int = LEVELS) -> np.ndarray:
     """One decode step of latent-space attention.
 
     q [B, n_q, d_h], packed [B, cap, ceil(G/2)] bytes, W_kv [2 n_kv d_h, G],
@@ -163,7 +183,8 @@ def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
       p = softmax(s)
       zbar = sum_t p_t z_t           (pool codes, Eq. 6)
       out = W_v,g zbar               (values decoded once, Eq. 6)
-    A sequence of length 0 gives out = 0. Returns float64 [B, n_q, d_h]."""
+    A sequence of length 0 gives out = 0. With L = levels per coordinate the
+    codes are b = log2 L bits wide and z = code - L/2. Returns float64 [B, n_q, d_h]."""
     q = np.asarray(q, dtype=np.float64)
     B, n_q, d_h = q.shape
     out = np.zeros((B, n_q, d_h), dtype=np.float64)
@@ -171,7 +192,7 @@ def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
         T = int(seq_lens[b])
         if T == 0:
             continue
-        Z = levels_of_codes(unpack_codes(packed[b, :T], G))        # [T, G]
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G, bits_of_levels(levels)), levels)   # [T, G]
         for h in range(n_q):
             Wk, Wv = decoder_blocks(W_kv, _kv_head(h, n_q, n_kv), n_kv, d_h)
             qt = Wk.T @ q[b, h]
@@ -183,7 +204,8 @@ def decode_attn(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
     return out
 
 
-def decode_attn_materialised(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np.ndarray:
+def decode_attn_materialised(q, packed, W_kv, seq_lens, n_kv: int, G: int,
+                             levels: int = LEVELS) -> np.ndarray:
     """The same step with keys and values written out, Eq. 5 without N_k and
     RoPE: K = Z W_k,g^T, V = Z W_v,g^T, then textbook softmax(K q / sqrt(d_h))^T V."""
     q = np.asarray(q, dtype=np.float64)
@@ -193,7 +215,7 @@ def decode_attn_materialised(q, packed, W_kv, seq_lens, n_kv: int, G: int) -> np
         T = int(seq_lens[b])
         if T == 0:
             continue
-        Z = levels_of_codes(unpack_codes(packed[b, :T], G))
+        Z = levels_of_codes(unpack_codes(packed[b, :T], G, bits_of_levels(levels)), levels)
         for h in range(n_q):
             Wk, Wv = decoder_blocks(W_kv, _kv_head(h, n_q, n_kv), n_kv, d_h)
             K = Z @ Wk.T

@@ -58,22 +58,23 @@ def normal_bf16(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
 
 
 # ----------------------------------------------------------- code-byte inputs
-def bytes_per_token(G: int) -> int:
-    """Storage width of one token's codes at 4 bits per coordinate."""
-    return (G * 4 + 7) // 8
+def bytes_per_token(G: int, bits: int = 4) -> int:
+    """Storage width of one token's codes at b bits per coordinate (4 by default)."""
+    return (G * bits + 7) // 8
 
 
-def uniform_code_bytes(g: np.random.Generator, shape_tokens, G: int) -> np.ndarray:
-    """Random cache bytes whose nibbles are i.i.d. uniform codes in 0..15.
+def uniform_code_bytes(g: np.random.Generator, shape_tokens, G: int, bits: int = 4) -> np.ndarray:
+    """Random cache bytes whose b-bit fields are i.i.d. uniform codes in 0..2^b - 1.
 
-    Two 4-bit codes share a byte, so uniform codes are uniform bytes. For odd G
-    the unused high nibble of each token's last byte is zero (the storage
-    convention of the packed cache)."""
-    P = bytes_per_token(G)
+    Codes share bytes, so uniform codes are uniform bytes. The unused high bits
+    of each token's last byte (when G b is not a multiple of 8) are zero, the
+    storage convention of the packed cache."""
+    P = bytes_per_token(G, bits)
     shape = tuple(np.atleast_1d(shape_tokens)) + (P,)
     out = g.integers(0, 256, size=shape, dtype=np.uint8)
-    if G % 2:
-        out[..., -1] &= 0x0F
+    used = G * bits - 8 * (P - 1)
+    if used < 8:
+        out[..., -1] &= np.uint8((1 << used) - 1)
     return out
 
 
@@ -100,10 +101,15 @@ class Workload:
     ragged: bool = False
     append_tokens: int = 0  # prefill chunk appended through E + FSQ (0 = none)
     codes_from_fsq: bool = False
+    levels: int = 16        # L levels per coordinate (4, 16 or 256: 2, 4 or 8 bits)
+
+    @property
+    def bits(self) -> int:
+        return {4: 2, 16: 4, 256: 8}[self.levels]
 
     @property
     def P(self) -> int:
-        return bytes_per_token(self.G)
+        return bytes_per_token(self.G, self.bits)
 
 
 WORKLOADS = {
@@ -115,6 +121,14 @@ WORKLOADS = {
                                   ragged=True),
     "qwen3_8b_g84_1m": Workload(4, "qwen3_8b_g84_1m", 36, 4096, 32, 8, 128, 84, 1, 1048576,
                                 codes_from_fsq=True),
+    # other operating points of the same shapes: G = 32 (256x, 16 B/token) and
+    # G = 20 (409.6x, 10 B/token) at 4 bits; the G = 84 byte budget (42 B) spent
+    # on 2-bit (L = 4, G = 168) or 8-bit (L = 256, G = 42) codes
+    "qwen3_8b_g32": Workload(5, "qwen3_8b_g32", 36, 4096, 32, 8, 128, 32, 1, 131072),
+    "qwen3_8b_g20": Workload(6, "qwen3_8b_g20", 36, 4096, 32, 8, 128, 20, 1, 131072),
+    "qwen3_8b_l4_g168": Workload(7, "qwen3_8b_l4_g168", 36, 4096, 32, 8, 128, 168, 1, 131072, levels=4),
+    "qwen3_8b_l256_g42": Workload(8, "qwen3_8b_l256_g42", 36, 4096, 32, 8, 128, 42, 1, 131072,
+                                  levels=256),
 }
 
 
@@ -151,7 +165,7 @@ def layer_x_chunk(w: Workload, layer: int, chunk: int, chunk_tokens: int = 8192)
 def layer_codes(w: Workload, layer: int, lens: np.ndarray | None = None, cap: int | None = None) -> np.ndarray:
     """Uniform cache bytes [batch, cap, P]; rows at t >= seq_lens[b] are zero."""
     cap = w.context if cap is None else cap
-    out = uniform_code_bytes(rng(w.wid, layer, T_CODES), (w.batch, cap), w.G)
+    out = uniform_code_bytes(rng(w.wid, layer, T_CODES), (w.batch, cap), w.G, w.bits)
     if lens is not None:
         for b, T in enumerate(lens):
             out[b, int(T):] = 0

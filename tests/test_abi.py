@@ -170,6 +170,24 @@ def test_decode_rope_validation_before_any_hip_call(args, status):
     assert rc == status
 
 
+@needs_lib
+@pytest.mark.parametrize("levels,status", [(8, fsq.FSQ_ERR_UNSUPPORTED), (2, fsq.FSQ_ERR_UNSUPPORTED),
+                                           (0, fsq.FSQ_ERR_UNSUPPORTED)])
+def test_levels_validation_before_any_hip_call(levels, status):
+    assert fsq.lib().fsq_append_levels(256, 256, 256, 4, 64, 8, levels, None) == status
+    rc = fsq.lib().fsq_decode_attn_levels(256, 256, 256, 256, 256, 1, 32, 8, 128, 256, levels, 16, 256,
+                                          1 << 20, None)
+    assert rc == status
+
+
+@needs_lib
+def test_levels_workspace_is_the_default_one():
+    # the 2- and 8-bit decode needs no more workspace than fsq_decode_workspace_bytes
+    ok = fsq.lib().fsq_decode_attn_levels(256, 256, 256, 256, 256, 1, 32, 8, 128, 84, 4, 1 << 20, 256,
+                                          64, None)
+    assert ok == fsq.FSQ_ERR_WORKSPACE
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(fsq, "_lib", None)
     monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")

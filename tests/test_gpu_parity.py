@@ -45,35 +45,37 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def check_codes(gpu_packed, x_bits, E_bits, G):
+def check_codes(gpu_packed, x_bits, E_bits, G, levels=16):
     """Compare GPU codes with the oracle's under the tie rule; return flip count."""
     x = synth.bf16_bits_to_f64(x_bits)
     E = synth.bf16_bits_to_f64(E_bits)
     u = orc.projection(x, E)
-    ref = orc.fsq_codes(u)
-    got = orc.unpack_codes(gpu_packed, G)
-    # the unused high nibble of an odd-G token must be zero
-    if G % 2:
-        assert np.all(gpu_packed[:, -1] >> 4 == 0)
+    bits = orc.bits_of_levels(levels)
+    ref = orc.fsq_codes(u, levels)
+    got = orc.unpack_codes(gpu_packed, G, bits)
+    # the unused high bits of a token's last byte must be zero
+    used = G * bits - 8 * (gpu_packed.shape[1] - 1)
+    if used < 8:
+        assert np.all(gpu_packed[:, -1] >> used == 0)
     diff = got.astype(int) - ref.astype(int)
     bad = np.nonzero(diff)
     n_bad = len(bad[0])
     assert np.all(np.abs(diff) <= 1), "a code differs by more than 1"
     assert n_bad <= max(1, int(FLIP_RATE * ref.size)), f"{n_bad} flipped codes"
     if n_bad:
-        ut = orc.fsq_bound(u[bad])
+        ut = orc.fsq_bound(u[bad], h=orc.H_BOUND if levels == 16 else orc.h_of_levels(levels))
         dist = np.abs(ut - (np.floor(ut) + 0.5))
         assert np.all(dist < TIE_TOL), f"flip away from a tie: {dist.max()}"
     return n_bad
 
 
-def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0):
+def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0, levels=16):
     n, C = x_bits.shape
     G = E_bits.shape[0]
-    P = orc.bytes_per_token(G)
+    P = orc.bytes_per_token(G, orc.bits_of_levels(levels))
     rows = n if dest_rows is None else dest_rows
     cache = torch.full((rows, P), 0xAB, dtype=torch.uint8, device="cuda")
-    fsq.fsq_append(dev_bf16(x_bits), dev_bf16(E_bits), cache[row0:row0 + n])
+    fsq.fsq_append(dev_bf16(x_bits), dev_bf16(E_bits), cache[row0:row0 + n], levels=levels)
     torch.cuda.synchronize()
     return cache.cpu().numpy()
 
@@ -89,6 +91,21 @@ def test_append_parity(fsq, n, C, G):
     E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
     got = run_append(fsq, x, E)
     check_codes(got, x, E, G)
+
+
+# L = 4 and 256 levels (2- and 8-bit codes): the vector (n < 32) and MFMA paths,
+# odd G and G not a multiple of the codes per byte
+@pytest.mark.parametrize("levels", [4, 256])
+@pytest.mark.parametrize("n,C,G", [
+    (1, 1024, 64), (5, 512, 83), (31, 4096, 84), (32, 1024, 64), (100, 520, 84), (257, 2048, 256),
+    (64, 8, 3), (40, 256, 42), (33, 512, 168),
+])
+def test_append_levels_parity(fsq, levels, n, C, G):
+    g = synth.rng(102, n + levels, C + G)
+    x = synth.normal_bf16(g, (n, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    got = run_append(fsq, x, E, levels=levels)
+    check_codes(got, x, E, G, levels)
 
 
 def test_append_into_cache_rows_keeps_other_rows(fsq):
@@ -153,6 +170,8 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     (2, 16, 4, 64, 30, 300, [300, 7]),           # G % 4 == 2: 4-byte W_v loads
     (1, 8, 2, 128, 131, 64, [64]),               # odd G: W_v vectors past the register set
     (1, 4, 1, 128, 130, 90, [90]),               # G % 4 == 2: the same with 2-wide vectors
+    (1, 32, 8, 128, 20, 131072, [131072]),       # G = 20 (409.6x, 10 B/token)
+    (1, 32, 8, 128, 32, 131072, [131000]),       # G = 32 (256x, 16 B/token)
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -282,6 +301,68 @@ def test_decode_rope_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens, theta):
         else:
             e = rel_l2(got[b], ref[b])
             assert e < REL_L2, (b, e)
+
+
+def run_decode_levels(fsq, q_bits, packed, W_bits, lens, n_kv, levels):
+    q = dev_bf16(q_bits)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_attn_levels(q, dev_u8(packed), dev_bf16(W_bits),
+                               torch.from_numpy(np.asarray(lens, np.int32)).cuda(), out, n_kv, levels)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# Decode over 2- and 8-bit code caches (L = 4, 256): aligned and unaligned
+# rows, odd G, ragged and empty sequences, long caches (the split kernel
+# streams them in several rounds), the same byte budget as G = 84 at 4 bits.
+@pytest.mark.parametrize("levels", [4, 256])
+@pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens", [
+    (1, 16, 8, 128, 64, 1024, [1024]),
+    (2, 32, 8, 128, 84, 1000, [1000, 257]),
+    (4, 16, 8, 128, 256, 600, [0, 1, 31, 600]),
+    (1, 8, 1, 64, 37, 130, [129]),
+    (1, 32, 8, 128, 128, 5000, [4999]),
+    (2, 32, 8, 128, 20, 3000, [3000, 17]),
+    (1, 32, 8, 128, 32, 70000, [70000]),
+])
+def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
+    g = synth.rng(210, levels, G + cap)
+    q = synth.normal_bf16(g, (B, n_q, d_h))
+    W = synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G))
+    bits = orc.bits_of_levels(levels)
+    packed = synth.uniform_code_bytes(g, (B, cap), G, bits)
+    lens = np.asarray(lens, np.int32)
+    got = run_decode_levels(fsq, q, packed, W, lens, n_kv, levels)
+    ref = orc.decode_attn(synth.bf16_bits_to_f64(q), packed, synth.bf16_bits_to_f64(W), lens, n_kv, G,
+                          levels=levels)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            e = rel_l2(got[b], ref[b])
+            assert e < REL_L2, (b, e)
+
+
+@pytest.mark.parametrize("levels,G", [(4, 168), (256, 42)])
+def test_levels_append_then_decode_at_the_g84_byte_budget(fsq, levels, G):
+    """42 bytes per token (the G = 84 budget) spent on 2- or 8-bit codes:
+    append 2000 tokens through the library, decode, compare with the oracle's
+    encode-then-decode."""
+    g = synth.rng(211, levels, G)
+    C, n_q, n_kv, d_h, T = 1024, 32, 8, 128, 2000
+    x = synth.normal_bf16(g, (T, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    W = synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G))
+    q = synth.normal_bf16(g, (1, n_q, d_h))
+    got_codes = run_append(fsq, x, E, levels=levels)
+    assert got_codes.shape[1] == 42
+    check_codes(got_codes, x, E, G, levels)
+    got = run_decode_levels(fsq, q, got_codes[None], W, [T], n_kv, levels)
+    bits = orc.bits_of_levels(levels)
+    ref_codes = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x), synth.bf16_bits_to_f64(E), levels), bits)
+    ref = orc.decode_attn(synth.bf16_bits_to_f64(q), ref_codes[None], synth.bf16_bits_to_f64(W), [T], n_kv, G,
+                          levels=levels)
+    assert rel_l2(got, ref) < REL_L2
 
 
 def test_decode_deterministic_and_split_invariant(fsq):
