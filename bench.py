@@ -361,12 +361,24 @@ def split_kernel_bytes(w, lens):
     return int(np.sum(lens)) * w.P
 
 
-def traffic_from_profile(w):
-    """HBM bytes per split-K launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+DECODE_SRC = ("decode.hip", "common.h", "decode_plan.h")
+APPEND_SRC = ("append.hip", "common.h", "append_gemv.h")
+
+
+def kernel_src_sha(files):
+    """sha256 over the kernel sources (under the package's csrc/, in order) that a
+    counter summary was taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_split_traffic_{w.name}.txt")
-    src = os.path.join(ROOT, "fsq_latent_decode_amd", "csrc", "decode.hip")
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "fsq_latent_decode_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def _profile_bytes(path, files):
+    """hbm_bytes_per_dispatch of a committed rocprofv3 counter summary, if it was
+    taken on the current sources; else None (the counters no longer describe the
+    kernel)."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -374,34 +386,22 @@ def traffic_from_profile(w):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if kv.get("decode_hip_sha256") != sha:
+    if kv.get("kernel_src_sha256") != kernel_src_sha(files):
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
+
+
+def traffic_from_profile(w):
+    """HBM bytes per split-K launch from the committed counter summary."""
+    return _profile_bytes(os.path.join(ROOT, "profiles", f"decode_split_traffic_{w.name}.txt"), DECODE_SRC)
 
 
 def traffic_from_append_profile(w):
-    """HBM bytes per prefill-append launch from the committed counter summary, if it
-    was taken on the current append kernel source; else None."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"append_prefill_traffic_{w.name}.txt")
-    src = os.path.join(ROOT, "fsq_latent_decode_amd", "csrc", "append.hip")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("append_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_dispatch"])
-    except (KeyError, ValueError):
-        return None
+    """HBM bytes per prefill-append launch from the committed counter summary."""
+    return _profile_bytes(os.path.join(ROOT, "profiles", f"append_prefill_traffic_{w.name}.txt"), APPEND_SRC)
 
 
 def sdpa_comparison(w, torch, fsq_ms, steps=10, warmup=3):
@@ -605,12 +605,15 @@ def summarize(w, ms, call_ms, replicas):
                              "t_roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3)},
            "replicas": replicas}
     if call_ms:
+        import fsq_latent_decode_amd as fsq
+        plan = fsq.decode_plan(w.batch, w.n_q, w.G, int(w.context))
         avg = float(np.mean(call_ms))
         nbytes = split_kernel_bytes(w, lens)
         ach = nbytes / (avg * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic_from_profile(w),
-                           "kernel": "decode_split_kernel", "bytes_per_launch": nbytes,
+                           "kernel": plan["kernel"], "splits_per_sequence": plan["splits"],
+                           "chunk_tokens": plan["chunk"], "bytes_per_launch": nbytes,
                            "avg_launch_us": avg * 1e3, "launches_timed": len(call_ms),
                            "timing": "hipExtLaunchKernelGGL start/stop events, eager steps"}
     return res

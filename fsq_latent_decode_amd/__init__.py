@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
-           "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels")
+           "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels", "fsq_decode_plan_info")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_step.restype = ctypes.c_int
         L.fsq_decode_attn_recon.argtypes = L.fsq_decode_attn.argtypes
         L.fsq_decode_attn_recon.restype = ctypes.c_int
+        L.fsq_decode_plan_info.argtypes = [i32, i32, i32, i64, vp, vp, vp]
+        L.fsq_decode_plan_info.restype = ctypes.c_int
         L.fsq_append_levels.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
         L.fsq_append_levels.restype = ctypes.c_int
         L.fsq_decode_attn_levels.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp, sz, vp]
@@ -132,6 +134,16 @@ def fsq_append(x: torch.Tensor, E: torch.Tensor, codes: torch.Tensor, stream=Non
 
 def decode_workspace_bytes(batch: int, n_q: int, G: int, seq_cap: int) -> int:
     return int(lib().fsq_decode_workspace_bytes(batch, n_q, G, seq_cap))
+
+
+def decode_plan(batch: int, n_q: int, G: int, seq_cap: int) -> dict:
+    """The split-K plan of fsq_decode_attn for these sizes: kernel name, chunks per
+    sequence and tokens per chunk."""
+    k, sp, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().fsq_decode_plan_info(batch, n_q, G, seq_cap, ctypes.byref(k), ctypes.byref(sp),
+                                      ctypes.byref(ch)), "fsq_decode_plan_info")
+    return {"kernel": "decode_stream_kernel" if k.value else "decode_split_kernel",
+            "splits": sp.value, "chunk": ch.value}
 
 
 def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -> torch.Tensor:

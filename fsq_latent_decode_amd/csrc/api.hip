@@ -53,6 +53,17 @@ int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_t
     return fsq_append_levels(x, E, codes, n_tokens, C, G, 16, stream);
 }
 
+int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap, int32_t *kernel,
+                         int32_t *splits, int64_t *chunk) {
+    if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return FSQ_ERR_SHAPE;
+    if (!kernel || !splits || !chunk) return FSQ_ERR_NULL;
+    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
+    *kernel = pl.stream;
+    *splits = pl.S;
+    *chunk = pl.chunk;
+    return FSQ_OK;
+}
+
 size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap) {
     if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return 0;
     return fsq::make_decode_plan(batch, n_q, G, seq_cap).total;

@@ -105,6 +105,16 @@ int fsq_append_levels(const uint16_t *x, const uint16_t *E, uint8_t *codes,
 size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap);
 
 /*
+ * fsq_decode_plan_info - how fsq_decode_attn (4-bit codes) splits a call of
+ * these sizes: *kernel = 0 for the round-synchronous split-K kernel (short
+ * chunks), 1 for the streaming split-K kernel (long chunks); *splits = chunks
+ * per sequence; *chunk = tokens per chunk. Host arithmetic only.
+ * Errors: FSQ_ERR_SHAPE (invalid sizes), FSQ_ERR_NULL (an output pointer NULL).
+ */
+int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap, int32_t *kernel,
+                         int32_t *splits, int64_t *chunk);
+
+/*
  * fsq_decode_attn - one decode step of attention read from the packed cache.
  *
  * For each sequence b and query head h (kv head g = h / (n_q / n_kv)), over

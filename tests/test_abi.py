@@ -188,6 +188,22 @@ def test_levels_workspace_is_the_default_one():
     assert ok == fsq.FSQ_ERR_WORKSPACE
 
 
+@needs_lib
+def test_decode_plan_host_logic():
+    # short caches: the round-synchronous split kernel; long ones: the streaming kernel
+    assert fsq.decode_plan(1, 32, 256, 32768)["kernel"] == "decode_split_kernel"
+    assert fsq.decode_plan(1, 32, 84, 131072)["kernel"] == "decode_split_kernel"
+    assert fsq.decode_plan(1, 32, 84, 1 << 20)["kernel"] == "decode_stream_kernel"
+    assert fsq.decode_plan(16, 16, 256, 65536)["kernel"] == "decode_stream_kernel"
+    for args in [(1, 32, 256, 1), (1, 32, 84, 1 << 20), (16, 16, 256, 65536), (3, 12, 37, 5000)]:
+        p = fsq.decode_plan(*args)
+        assert p["splits"] * p["chunk"] >= args[3] > (p["splits"] - 1) * p["chunk"]
+        assert p["splits"] <= 1024 and p["chunk"] % 128 == 0
+    assert fsq.decode_plan(1, 32, 256, 0)["splits"] == 0
+    with pytest.raises(fsq.FsqError):
+        fsq.decode_plan(0, 32, 256, 10)
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(fsq, "_lib", None)
     monkeypatch.setattr(fsq, "_LIB_PATH", "/nonexistent/libfsq.so")
