@@ -111,3 +111,83 @@ def test_rope_decode_differs_from_plain_keys_and_zero_length():
     b = orc.decode_attn(q, packed, W, [40, 0], 2, 12)
     assert rel(a[0], b[0]) > 1e-3          # norm and rotation change the scores
     assert np.all(a[1] == 0)
+
+
+# --------------------------------------------------------------- mutants
+def _rope_pins_hold(rope_fn):
+    """The closed-form RoPE pins above, as one predicate over a rope function."""
+    for t in [1, 3, 17]:
+        out = rope_fn(np.array([[1.0, 0.0], [0.0, 1.0]]), [t, t], 1e6)
+        if not (np.allclose(out[0], [math.cos(t), math.sin(t)], atol=1e-12)
+                and np.allclose(out[1], [-math.sin(t), math.cos(t)], atol=1e-12)):
+            return False
+    k, t = np.array([[1.0, 2.0, 3.0, 4.0]]), 7
+    a0, a1 = t, t / 10.0
+    exp = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+           3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+    return bool(np.allclose(rope_fn(k, [t], 100.0)[0], exp, atol=1e-12))
+
+
+def _rope_interleaved(k, positions, theta):
+    # pairs (2i, 2i + 1) instead of (i, i + d_h/2)
+    k = np.asarray(k, dtype=np.float64)
+    d_h = k.shape[-1]
+    inv = theta ** (-2.0 * np.arange(d_h // 2) / d_h)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    a, b = k[..., 0::2], k[..., 1::2]
+    out = np.empty_like(k)
+    out[..., 0::2] = a * np.cos(ang) - b * np.sin(ang)
+    out[..., 1::2] = b * np.cos(ang) + a * np.sin(ang)
+    return out
+
+
+def _rope_mutant(kind):
+    def fn(k, positions, theta):
+        k = np.asarray(k, dtype=np.float64)
+        d_h = k.shape[-1]
+        half = d_h // 2
+        e = np.arange(half, dtype=np.float64)
+        inv = theta ** (-(e if kind == "freq_exponent" else 2.0 * e) / d_h)
+        ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+        c, s = np.cos(ang), np.sin(ang)
+        if kind == "sign":
+            s = -s
+        a, b = k[..., :half], k[..., half:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+    return fn
+
+
+def test_rope_pins_hold_for_the_oracle():
+    assert _rope_pins_hold(orc.rope)
+
+
+@pytest.mark.parametrize("kind", ["interleaved", "sign", "freq_exponent"])
+def test_rope_pins_catch_planted_mistakes(kind):
+    fn = _rope_interleaved if kind == "interleaved" else _rope_mutant(kind)
+    assert not _rope_pins_hold(fn)
+
+
+def _rms_pins_hold(fn):
+    g = np.random.default_rng(3)
+    k = g.standard_normal((4, 64)) * 3.0
+    ms = np.mean(k * k, axis=1)
+    gam = g.standard_normal(64)
+    return bool(np.allclose(np.mean(fn(k, np.ones(64), 1e-6) ** 2, axis=1), ms / (ms + 1e-6), rtol=1e-13)
+                and np.allclose(fn(k, gam, 0.0) / fn(k, np.ones(64), 0.0), gam))
+
+
+@pytest.mark.parametrize("kind", ["sum_not_mean", "no_gamma", "eps_outside", "gamma_inverted"])
+def test_rms_norm_pins_catch_planted_mistakes(kind):
+    def fn(k, gamma, eps):
+        k = np.asarray(k, dtype=np.float64)
+        gamma = np.asarray(gamma, dtype=np.float64)
+        if kind == "sum_not_mean":
+            return k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps) * gamma
+        ms = np.mean(k * k, axis=-1, keepdims=True)
+        if kind == "no_gamma":
+            return k / np.sqrt(ms + eps)
+        if kind == "eps_outside":
+            return k / (np.sqrt(ms) + eps) * gamma
+        return k / np.sqrt(ms + eps) / gamma
+    assert _rms_pins_hold(orc.rms_norm)
+    assert not _rms_pins_hold(fn)
