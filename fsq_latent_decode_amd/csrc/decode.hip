@@ -301,6 +301,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     int64_t c1 = (c0 + chunk < seq_cap) ? c0 + chunk : seq_cap;
     const int t = lane & 31, hh = lane >> 5;
     const uint8_t *seq = codes + (size_t)b * seq_cap * P;
+    // the sequence length is requested first and used after the Q~ barrier
+    const int32_t T_raw = seq_lens[b];
 
     // ---- per-lane loads of one tile (this lane's half of token t)
     uint32_t ld[NLD];
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         __syncthreads();
         // the sequence length: leave if this chunk is past it (uniform), else
         // bound the chunk and recount the first round's tokens
-        int64_t T = seq_lens[b];
+        int64_t T = T_raw;
         T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
         if (c0 >= T) return;
         c1 = (c0 + chunk < T) ? c0 + chunk : T;
@@ -722,6 +724,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     int64_t cend = (c0 + chunk < seq_cap) ? c0 + chunk : seq_cap;
     const int t = lane & 31, hh = lane >> 5;
     const uint8_t *seq = codes + (size_t)b * seq_cap * P;
+    // the sequence length is requested first and used once Q~ is in LDS
+    const int32_t T_raw = seq_lens[b];
     uint8_t *ring = ring_lds + wave * D * SLOTB;
     uint8_t *tile = tile_lds + wave * 32 * TS;
 
@@ -758,7 +762,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // Q~ rows of this head group -> LDS (rows padded to GP + 8 halves) -> each
     // lane's B operands, as in the split kernel. Only the first tile is loaded
     // alongside (the compiler waits for all loads before the Q~ stores); the
-    // ring's other D - 2 tiles are issued once Q~ is in place.
+    // ring's other D - 2 tiles are issued once Q~ is in place, so they are in
+    // flight while the first tile is processed.
     issue(0);
     half8 qv[RC ? 1 : KB];
     half8 qb[RC ? 4 : 1][2];   // RC: B operands q[head][d] * scale per 32-row block of d and half
@@ -802,7 +807,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
                     qb[db][e][jj] = (_Float16)(ok ? x : 0.0f);
                 }
         lds_barrier();
-        int64_t T = seq_lens[b];
+        int64_t T = T_raw;
         T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
         if (c0 >= T) {   // uniform: nothing to do; no load may still target the LDS
             __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -830,7 +835,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
             *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
         }
         lds_barrier();
-        int64_t T = seq_lens[b];
+        int64_t T = T_raw;
         T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
         if (c0 >= T) {   // uniform: nothing to do; no load may still target the LDS
             __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -1107,172 +1112,234 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
 }
 
 // ----------------------------------------------------------------- merge
-// One CTA per (head, sequence): M = max_i m_i, c_i = l_i 2^(m_i - M),
-// zbar = sum_i c_i zbar_i / sum_i c_i, out = W_v,g zbar. Every global load (the
-// (m, l) pairs, the first 16 partial rows per thread, and this thread's part of
-// its W_v row, VW bf16 per load) is issued before any is used.
-constexpr int kMergeRows = 16;        // partial rows per thread per batch
-constexpr int kMergeMl = 4;           // (m, l) pairs per thread: S <= 1024
+// One CTA of 16 waves per (head, sequence): out = W_v,g zbar with
+//   zbar = sum_i c_i zbar_i / sum_i c_i,  c_i = l_i 2^(m_i - M),  M = max_i m_i.
+// Every global load (this thread's part of its W_v row, VW bf16 per load, and R
+// partial rows per thread with their (m, l)) is issued before any is used; 16
+// waves keep more of them in flight per CU than 4 would, which is what bounds
+// this kernel. The sum is taken in two levels, each against its own reference
+// max, so only two barriers are needed: a thread (8-position group kg, split
+// group sg: rows sg + u SG) sums its rows against their max m_sg; TPP threads
+// per position then sum the split groups against their own max and combine by
+// shuffles. With few heads, blockIdx.z = c of NC CTAs per head each apply rows
+// [c d_h / NC, (c + 1) d_h / NC) of W_v (zbar is formed by each of them).
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeMaxS = 1024;
 
-template <int VW>
-__global__ __launch_bounds__(256) void decode_merge_kernel(
+template <int VW, int R>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
     int chunk, int S, int natural, int bits) {
     using VT = typename VecT<VW>::T;
-    // W_v vectors per thread held in registers (two or more threads per row);
-    // narrow vectors (odd G) beyond 32 per thread are read in the dot loop
-    constexpr int NVT = (kMaxG / VW / 2) < 32 ? (kMaxG / VW / 2) : 32;
-    __shared__ float coef[kMergeMl * 256];
-    __shared__ float zpart[256 * 8];   // [split group][GP]
+    // W_v vectors per thread: a row is shared by TPR >= 4 threads (d_h <= 256),
+    // so at most NVA per thread; NVT of them (at most 32 VGPRs) are held from the
+    // start, the rest (narrow vectors only) are read in the dot loop
+    constexpr int NVA = (kMaxG / VW + 3) / 4;
+    constexpr int NVR = VW >= 4 ? 8 : 16;
+    constexpr int NVT = NVA < NVR ? NVA : NVR;
+    __shared__ __attribute__((aligned(16))) float zpart[9216];   // [split group][ZS]: ZS * SG <= 9216
+    __shared__ float gm[256], gl[256];                            // per split group: SG <= 256
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
-    __shared__ float red[8];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
+    const int DR = d_h / (int)gridDim.z, d0 = (int)blockIdx.z * DR;   // this CTA's rows of W_v
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
     const size_t srow = (size_t)n_q;   // rows between splits
-
-    // The loads below are issued over all S splits of the workspace (indices
-    // clamped to S - 1) before the sequence length arrives; entries of splits
-    // at or past the sequence's split count ns are discarded by selects.
-    // ---- issue: (m, l) pairs
-    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (size_t)b * S * n_q + h;
-    float2 mlr[kMergeMl];
+    // The sequence length is read first; the loads below are issued over all S
+    // splits of the workspace (indices clamped) before it arrives, and entries
+    // of splits at or past the sequence's split count ns are discarded by selects.
+    const int32_t T_raw = seq_lens[b];
+    // ---- issue: W_v row d, vectors part, part + TPR, ... (first: W_v is the
+    // coldest data, read from HBM, while the partials were just written)
+    const int g = h / (n_q / n_kv);
+    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
+    int TPR = 4;
+    while (TPR * 2 * DR <= kMergeThreads && TPR < 64) TPR *= 2;
+    const int NV = G / VW;
+    const int d = d0 + tid / TPR, part = tid % TPR;
+    const bool drow = tid / TPR < DR;
+    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
+    VT wv[NVT];
 #pragma unroll
-    for (int u = 0; u < kMergeMl; ++u) {
-        const int i = tid + 256 * u;
-        mlr[u] = ml[(size_t)(i < S ? i : S - 1) * srow];
+    for (int i = 0; i < NVT; ++i) {
+        const int vi = part + TPR * i;
+        if (vi < NV) wv[i] = wrow[vi];   // others unused
     }
-    // ---- issue: first batch of partial rows (thread = 8-position group kg, split group sg)
-    const int KG = GP / 8, SG = 256 / KG;
+    // ---- issue: partial rows sg + u SG and their (m, l)
+    const int KG = GP / 8, SG = kMergeThreads / KG;
+    // level 2 uses TPP threads per position; zpart rows are padded to ZS floats,
+    // ZS = 64 / TPP (mod 32), so a wave's 64 reads fall on distinct bank pairs
+    const int TPP = GP <= 32 ? 32 : GP <= 64 ? 16 : GP <= 128 ? 8 : 4;
+    const int ZS = GP + (TPP == 32 ? 4 : 64 / TPP);
     const int kg = tid % KG, sg = tid / KG;
     const bool zthr = sg < SG;
     const _Float16 *zp = part_z + ((size_t)b * S * n_q + h) * GP + kg * 8;
-    half8 v[kMergeRows];
+    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (size_t)b * S * n_q + h;
+    half8 v[R];
+    float2 mr[R];
 #pragma unroll
-    for (int u = 0; u < kMergeRows; ++u) {
-        const int i = sg + u * SG;
-        v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(zthr && i < S ? i : 0) * srow * GP);
+    for (int u = 0; u < R; ++u) {
+        const int i = sg + u * SG, ic = zthr && i < S ? i : 0;
+        v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)ic * srow * GP);
+        mr[u] = ml[(size_t)ic * srow];
     }
-    // ---- issue: W_v row d, vectors part, part + TPR, ... (TPR >= 2 threads per row)
-    const int g = h / (n_q / n_kv);
-    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
-    int TPR = 2;
-    while (TPR * 2 * d_h <= 256 && TPR < 16) TPR *= 2;
-    const int NV = G / VW;
-    const bool reg_path = 2 * d_h <= 256;   // every row covered by >= 2 threads in one pass
-    const int d = tid / TPR, part = tid % TPR;
-    const bool drow = reg_path && d < d_h;
-    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
-    VT wv[NVT];
-    if (reg_path) {
-#pragma unroll
-        for (int i = 0; i < NVT; ++i) {
-            const int vi = part + TPR * i;
-            wv[i] = wrow[vi < NV ? vi : NV - 1];
-        }
-    }
-
-    int64_t T = seq_lens[b];
+    int64_t T = T_raw;
     T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
     const int ns = (int)((T + chunk - 1) / chunk);
-
-    // ---- M and L over the sequence's splits (the (m, l) loads are the oldest in flight)
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kMergeMl; ++u)
-        if (tid + 256 * u < ns) M = fmaxf(M, mlr[u].x);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0) red[wave] = M;
-    __syncthreads();
     if (ns == 0) {   // empty sequence (uniform): the output is zero
-        for (int d = tid; d < d_h; d += blockDim.x) o[d] = 0;
+        for (int dd = tid; dd < DR; dd += kMergeThreads) o[d0 + dd] = 0;
         return;
     }
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float Lp = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kMergeMl; ++u) {
-        const int i = tid + 256 * u;
-        if (i < ns) {
-            const float c = mlr[u].y * __builtin_amdgcn_exp2f(mlr[u].x - M);
-            coef[i] = c;
-            Lp += c;
-        }
-    }
-    for (int off = 32; off > 0; off >>= 1) Lp += __shfl_xor(Lp, off);
-    if (lane == 0) red[4 + wave] = Lp;
-    __syncthreads();
-    const float invL = 1.0f / ((red[4] + red[5]) + (red[6] + red[7]));
 
-    // ---- weighted sum of the partial rows
-    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // ---- level 1: this thread's rows against their own max
     if (zthr) {
+        float m = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kMergeRows; ++u) {
-            const int i = sg + u * SG;
-            const bool ok = i < ns;
-            const float c = coef[ok ? i : 0];
+        for (int u = 0; u < R; ++u)
+            if (sg + u * SG < ns) m = fmaxf(m, mr[u].x);
+        float a[8] = {0, 0, 0, 0, 0, 0, 0, 0}, l = 0.0f;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            // rows of splits past the sequence's end hold stale workspace
+            // contents (possibly not finite): selected out, not multiplied by 0
+            const bool ok = sg + u * SG < ns;
+            const float c = ok ? mr[u].y * __builtin_amdgcn_exp2f(mr[u].x - m) : 0.0f;
+            l += c;
 #pragma unroll
             for (int j = 0; j < 8; ++j) a[j] += ok ? c * (float)v[u][j] : 0.0f;
         }
-        for (int i0 = sg + kMergeRows * SG; i0 < ns; i0 += kMergeRows * SG) {   // long caches
+        for (int i0 = sg + R * SG; i0 < ns; i0 += R * SG) {   // more splits than one batch covers
 #pragma unroll
-            for (int u = 0; u < kMergeRows; ++u) {
-                const int i = i0 + u * SG;
-                v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)(i < ns ? i : ns - 1) * srow * GP);
+            for (int u = 0; u < R; ++u) {
+                const int i = i0 + u * SG, ic = i < ns ? i : ns - 1;
+                v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)ic * srow * GP);
+                mr[u] = ml[(size_t)ic * srow];
             }
+            float mb = m;
 #pragma unroll
-            for (int u = 0; u < kMergeRows; ++u) {
-                const int i = i0 + u * SG;
-                const float c = i < ns ? coef[i] : 0.0f;
+            for (int u = 0; u < R; ++u)
+                if (i0 + u * SG < ns) mb = fmaxf(mb, mr[u].x);
+            const float alpha = __builtin_amdgcn_exp2f(m - mb);   // m is finite here (row sg < ns)
+            l *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] *= alpha;
+            m = mb;
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const float c = i0 + u * SG < ns ? mr[u].y * __builtin_amdgcn_exp2f(mr[u].x - m) : 0.0f;
+                l += c;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) a[j] += c * (float)v[u][j];
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) zpart[sg * GP + kg * 8 + j] = a[j];
+        for (int j = 0; j < 8; ++j) zpart[sg * ZS + kg * 8 + j] = a[j];
+        if (kg == 0) {
+            gm[sg] = m;   // -inf: no rows of the sequence in this group (l = 0, a = 0)
+            gl[sg] = l;
+        }
     }
     __syncthreads();
-    for (int p = tid; p < GP; p += blockDim.x) {
-        float z = 0.0f;
-        for (int u = 0; u < SG; ++u) z += zpart[u * GP + p];
-        zbar[natural ? p : pos_to_coord(p, GP, bits)] = z * invL;
+    // ---- level 2: TPP threads per position (TPP GP <= 1024), split groups
+    // r + TPP k, k < SG / TPP <= kL2 (all LDS reads issued before use)
+    {
+        constexpr int kL2 = 16;   // SG / TPP <= 13 for every GP
+        const int p = tid / TPP, r = tid % TPP;
+        const int pc = p < GP ? p : 0;
+        float gv[kL2], lv[kL2], zv[kL2];
+#pragma unroll
+        for (int k = 0; k < kL2; ++k) {
+            const int uc = r + TPP * k < SG ? r + TPP * k : 0;
+            gv[k] = gm[uc];
+            lv[k] = gl[uc];
+            zv[k] = zpart[uc * ZS + pc];
+        }
+#pragma unroll
+        for (int k = 0; k < kL2; ++k)
+            if (r + TPP * k >= SG) gv[k] = -INFINITY;
+        float m = gv[0];
+#pragma unroll
+        for (int k = 1; k < kL2; ++k) m = fmaxf(m, gv[k]);
+        float z = 0.0f, l = 0.0f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < kL2; ++k) {
+                const float c = __builtin_amdgcn_exp2f(gv[k] - m);   // 0 for empty groups
+                z += c * zv[k];
+                l += c * lv[k];
+            }
+        }
+        float M = m;
+        for (int off = 1; off < TPP; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));   // finite: split 0 is in group 0
+        const float e = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        z *= e;
+        l *= e;
+        for (int off = 1; off < TPP; off <<= 1) {
+            z += __shfl_xor(z, off);
+            l += __shfl_xor(l, off);
+        }
+        if (p < GP && r == 0) zbar[natural ? p : pos_to_coord(p, GP, bits)] = z / l;
     }
     __syncthreads();
 
     // ---- out = W_v,g zbar
-    if (reg_path) {
-        float acc = 0.0f;
+    float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NVT; ++i) {
-            const int vi = part + TPR * i;
-            float wf[VW];
-            bf16_vec_to_f32<VW>(wv[i], wf);
-            if (vi < NV) {
-#pragma unroll
-                for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
-            }
-        }
-        for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
-            float wf[VW];
-            bf16_vec_to_f32<VW>(wrow[vi], wf);
+    for (int i = 0; i < NVT; ++i) {
+        const int vi = part + TPR * i;
+        float wf[VW];
+        bf16_vec_to_f32<VW>(wv[i], wf);
+        if (vi < NV) {
 #pragma unroll
             for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
         }
-        for (int off = TPR >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (part == 0 && drow) o[d] = f32_to_bf16(acc);
-    } else {
-        // d_h > 128: one thread per row, loads in the loop
-        for (int dd = tid; dd < d_h; dd += blockDim.x) {
-            float acc = 0.0f;
-            const uint16_t *row = Wv + (size_t)dd * G;
-#pragma unroll 8
-            for (int k = 0; k < G; ++k) acc += bf16_to_f32(row[k]) * zbar[k];
-            o[dd] = f32_to_bf16(acc);
-        }
     }
+    for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
+        float wf[VW];
+        bf16_vec_to_f32<VW>(wrow[vi], wf);
+#pragma unroll
+        for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
+    }
+    for (int off = TPR >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == 0 && drow) o[d] = f32_to_bf16(acc);
+}
+
+// Merge launch: the widest bf16 vector that divides G and the W_kv alignment,
+// and the fewest partial rows per thread that cover S in one batch (at most 8).
+static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint16_t *W_kv,
+                               const int32_t *seq_lens, uint16_t *out, int64_t seq_cap, int G,
+                               int GP, int n_q, int n_kv, int d_h, int batch, int chunk, int S,
+                               int natural, int bits, hipStream_t st) {
+    if (S < 1 || S > kMergeMaxS || GP > kMaxG || d_h > kMaxDh) return hipErrorInvalidValue;
+    const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
+                   : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
+                   : ((G & 1) == 0 && ((uintptr_t)W_kv & 3) == 0) ? 2
+                                                                   : 1;
+    const int SG = kMergeThreads / (GP / 8);
+    const int rows = (S + SG - 1) / SG;
+    const int r = rows <= 2 ? 2 : rows <= 4 ? 4 : 8;   // more: the kernel loops
+    // NC CTAs per head while the grid stays within 256 CTAs and each applies
+    // at least 16 rows of W_v
+    int nc = 1;
+    while (nc < 4 && (int64_t)n_q * batch * nc * 2 <= 256 && d_h % (nc * 2) == 0 && d_h / (nc * 2) >= 16) nc *= 2;
+    const dim3 mg(n_q, batch, nc);
+#define FSQ_MERGE_CASE(VWX, RX)                                                                           \
+    if (vw == VWX && r == RX) {                                                                           \
+        decode_merge_kernel<VWX, RX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out, seq_cap, \
+                                                                   G, GP, n_q, n_kv, d_h, chunk, S,       \
+                                                                   natural, bits);                        \
+        return hipGetLastError();                                                                         \
+    }
+#define FSQ_MERGE_VW(VWX) FSQ_MERGE_CASE(VWX, 2) FSQ_MERGE_CASE(VWX, 4) FSQ_MERGE_CASE(VWX, 8)
+    FSQ_MERGE_VW(8)
+    FSQ_MERGE_VW(4)
+    FSQ_MERGE_VW(2)
+    FSQ_MERGE_VW(1)
+#undef FSQ_MERGE_VW
+#undef FSQ_MERGE_CASE
+    return hipErrorInvalidValue;
 }
 
 template <int GP, int NW, int BITS>
@@ -1429,16 +1496,8 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         }
         if (e != hipSuccess) return e;
     }
-    const dim3 mg(n_q, batch);
-#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, pl.chunk, pl.S, pl.stream, bits
-    switch (vw) {
-        case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        case 2: decode_merge_kernel<2><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        default: decode_merge_kernel<1><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS);
-    }
-#undef FSQ_MERGE_ARGS
-    return hipGetLastError();
+    return launch_merge(pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, batch, pl.chunk,
+                        pl.S > 0 ? pl.S : 1, pl.stream, bits, st);
 }
 
 // The key-reconstruction comparison: no absorption launch; the split kernel
@@ -1497,21 +1556,9 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
         }
         if (e != hipSuccess) return e;
     }
-    const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
-                   : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
-                   : ((G & 1) == 0 && ((uintptr_t)W_kv & 3) == 0) ? 2
-                                                                   : 1;
-    const dim3 mg(n_q, batch);
     const int chunk_i = S > 0 ? (int)chunk : pl.chunk;
-#define FSQ_MERGE_ARGS pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, chunk_i, (S > 0 ? S : 1), 1, 4
-    switch (vw) {
-        case 8: decode_merge_kernel<8><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        case 4: decode_merge_kernel<4><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        case 2: decode_merge_kernel<2><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS); break;
-        default: decode_merge_kernel<1><<<mg, 256, 0, st>>>(FSQ_MERGE_ARGS);
-    }
-#undef FSQ_MERGE_ARGS
-    return hipGetLastError();
+    return launch_merge(pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, batch, chunk_i,
+                        S > 0 ? S : 1, 1, 4, st);
 }
 
 }  // namespace fsq
