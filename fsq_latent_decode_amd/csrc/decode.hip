@@ -514,11 +514,12 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const float zscale = kCodeScale / l_run;   // codes n * 2^-24 pooled: zbar = 2^24 acc / l - L/2
     constexpr float kLevelOffset = (float)(1 << (BITS - 1));
     const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
-    const size_t pbase = ((size_t)b * S + s) * n_q + hg * 32;
+    // partials are head-major: row ((b n_q + h) S + s), so a head's rows are contiguous
+    const size_t pbase = ((size_t)b * n_q + hg * 32) * S + s;
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     if (t < heads) {
-        _Float16 *dst = part_z + (pbase + t) * GP;
+        _Float16 *dst = part_z + (pbase + (size_t)t * S) * GP;
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
             const int cb = wv + NW * j;
@@ -535,8 +536,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         }
     }
     if (wave == 0 && lane < heads) {
-        part_ml[(pbase + lane) * 2 + 0] = m_ref;
-        part_ml[(pbase + lane) * 2 + 1] = l_run;
+        part_ml[(pbase + (size_t)lane * S) * 2 + 0] = m_ref;
+        part_ml[(pbase + (size_t)lane * S) * 2 + 1] = l_run;
     }
 }
 
@@ -1063,7 +1064,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     const float cw = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
     const float zscale = kCodeScale / L;
     const int heads = RC ? grp : ((n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32);
-    const size_t pbase = ((size_t)b * S + s) * n_q + hg * (RC ? grp : 32);
+    const size_t pbase = ((size_t)b * n_q + hg * (RC ? grp : 32)) * S + s;   // head-major partial rows
     floatx4 *cbuf = reinterpret_cast<floatx4 *>(ring_lds);   // [block][wave][4][64 lanes]
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -1091,7 +1092,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sum[e] += cbuf[((i * NW + w) * 4 + e) * 64 + lane];
                 if (t < heads) {
-                    _Float16 *dst = part_z + (pbase + t) * GP + cb * 32 + hh * 4;
+                    _Float16 *dst = part_z + (pbase + (size_t)t * S) * GP + cb * 32 + hh * 4;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const half4 v = {(_Float16)fmaf(sum[e][0], zscale, -8.0f),
@@ -1106,8 +1107,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         lds_barrier();
     }
     if (wave == 0 && lane < heads) {
-        part_ml[(pbase + lane) * 2 + 0] = M;
-        part_ml[(pbase + lane) * 2 + 1] = L;
+        part_ml[(pbase + (size_t)lane * S) * 2 + 0] = M;
+        part_ml[(pbase + (size_t)lane * S) * 2 + 1] = L;
     }
 }
 
@@ -1146,7 +1147,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int tid = threadIdx.x;
     const int DR = d_h / (int)gridDim.z, d0 = (int)blockIdx.z * DR;   // this CTA's rows of W_v
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
-    const size_t srow = (size_t)n_q;   // rows between splits
+    const size_t srow = 1;   // rows between splits (head-major partials)
     // The sequence length is read first; the loads below are issued over all S
     // splits of the workspace (indices clamped) before it arrives, and entries
     // of splits at or past the sequence's split count ns are discarded by selects.
@@ -1175,8 +1176,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int ZS = GP + (TPP == 32 ? 4 : 64 / TPP);
     const int kg = tid % KG, sg = tid / KG;
     const bool zthr = sg < SG;
-    const _Float16 *zp = part_z + ((size_t)b * S * n_q + h) * GP + kg * 8;
-    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (size_t)b * S * n_q + h;
+    const _Float16 *zp = part_z + ((size_t)b * n_q + h) * S * GP + kg * 8;
+    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + ((size_t)b * n_q + h) * S;
     half8 v[R];
     float2 mr[R];
 #pragma unroll
