@@ -138,12 +138,14 @@ def decode_workspace_bytes(batch: int, n_q: int, G: int, seq_cap: int) -> int:
 
 def decode_plan(batch: int, n_q: int, G: int, seq_cap: int) -> dict:
     """The split-K plan of fsq_decode_attn for these sizes: kernel name, chunks per
-    sequence and tokens per chunk."""
+    sequence and tokens per chunk (with device_split, the split is chosen on the
+    device from the actual lengths: at most that many chunks of at least that
+    many tokens)."""
     k, sp, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
     _check(lib().fsq_decode_plan_info(batch, n_q, G, seq_cap, ctypes.byref(k), ctypes.byref(sp),
                                       ctypes.byref(ch)), "fsq_decode_plan_info")
     return {"kernel": "decode_stream_kernel" if k.value else "decode_split_kernel",
-            "splits": sp.value, "chunk": ch.value}
+            "device_split": k.value == 2, "splits": sp.value, "chunk": ch.value}
 
 
 def alloc_workspace(batch: int, n_q: int, G: int, seq_cap: int, device="cuda") -> torch.Tensor:

@@ -58,7 +58,7 @@ int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap,
     if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (!kernel || !splits || !chunk) return FSQ_ERR_NULL;
     const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
-    *kernel = pl.stream;
+    *kernel = pl.stream ? (pl.dyn ? 2 : 1) : 0;
     *splits = pl.S;
     *chunk = pl.chunk;
     return FSQ_OK;

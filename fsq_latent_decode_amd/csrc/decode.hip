@@ -690,12 +690,42 @@ __device__ inline half8 unpack_codes_centered(uint32_t w) {
     return __builtin_bit_cast(half8, t) - half8{c, c, c, c, c, c, c, c};
 }
 
+// Device-side split of the streaming kernel (kDynMaxBatch sequences or fewer):
+// the chunk is chosen from the actual lengths, so that the sum of all
+// sequences' tokens spreads over ncta CTAs in whole rounds of kStreamWaves
+// tiles, at least chunk_min (which bounds a sequence's split count by the
+// workspace's). Sequence b then has ceil(T_b / chunk) work items, numbered
+// consecutively over the sequences; CTA i takes item i. Every wave of a CTA
+// computes this the same way: lane b holds T_b (one vector load), a wave sum
+// gives the total, a prefix scan of the item counts locates item i.
+__device__ inline int stream_dyn_chunk(int64_t total, int ncta, int chunk_min) {
+    constexpr int64_t q = 32 * kStreamWaves;
+    int64_t c = (total + ncta - 1) / ncta;
+    c = (c + q - 1) / q * q;
+    return (int)(c < chunk_min ? chunk_min : c);
+}
+__device__ inline int64_t wave_sum64(int64_t v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+// lane's clamped length T_lane (0 past the batch) and the chunk
+__device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int batch, int64_t seq_cap,
+                                      int ncta, int chunk_min, int lane, int64_t &t_lane) {
+    int64_t T = lane < batch ? (int64_t)seq_lens[lane] : 0;
+    T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
+    t_lane = T;
+    return stream_dyn_chunk(wave_sum64(T), ncta, chunk_min);
+}
+
 template <int GP, int NW, int D, bool AL, int RC>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 3)))) void decode_stream_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
-    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S,
-    ReconArgs ra) {
+    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk_arg, int S,
+    int dyn_batch, int ncta, ReconArgs ra) {
+    // dyn_batch > 0: device-side split (stream_dyn_lens), 1-D grid of CTAs over
+    // work items; chunk_arg is then the smallest chunk. Otherwise CTA (s, b)
+    // takes tokens [s chunk_arg, (s + 1) chunk_arg) of sequence b.
     using C = StreamCfg<GP, NW, D, AL>;
     constexpr int KB = C::KB, CB = C::CB, TS = C::TS, SLOTB = C::SLOTB, NI = C::NI;
     // scores arrive in units of 2^-24 from absorbed queries (codes as fp16
@@ -719,14 +749,68 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     const int P = (G + 1) / 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int s = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int hg = blockIdx.z;
+    // Q~ rows of head group hg of a sequence (32 x GP fp16, contiguous): NQI
+    // 16-byte loads per thread, issued first for the sequence known before the
+    // split is (the only one of a one-sequence call, or CTA row blockIdx.y) and
+    // again once it is known if it differs
+    constexpr int QROW = GP + 8;
+    constexpr int NQ16 = 32 * GP / 8;
+    constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
+    u32x4 qreg[RC ? 1 : NQI];
+    auto load_q = [&](int bq) {
+        if constexpr (!RC) {
+            const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)bq * nqp + hg * 32) * GP);
+#pragma unroll
+            for (int u = 0; u < NQI; ++u) {
+                const int i = threadIdx.x + u * NW * 64;
+                qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
+            }
+        }
+    };
+    const int b_early = dyn_batch > 0 ? 0 : (int)blockIdx.y;
+    load_q(b_early);
+    int s, b, chunk;
+    int64_t T_dyn = 0;
+    if (dyn_batch == 1) {   // one sequence: item i is chunk i of it
+        int64_t T0 = seq_lens[0];
+        T0 = T0 < 0 ? 0 : (T0 > seq_cap ? seq_cap : T0);
+        chunk = stream_dyn_chunk(T0, ncta, chunk_arg);
+        b = 0;
+        s = blockIdx.x;
+        if ((int64_t)s * chunk >= T0) return;   // no work left (uniform)
+        T_dyn = T0;
+    } else if (dyn_batch > 0) {
+        int64_t t_lane;
+        chunk = stream_dyn_lens(seq_lens, dyn_batch, seq_cap, ncta, chunk_arg, lane, t_lane);
+        const int n = (int)((t_lane + chunk - 1) / chunk);   // this lane's sequence's items
+        int incl = n;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        const int item = blockIdx.x;
+        b = __builtin_popcountll(__ballot(incl <= item));   // sequences wholly before the item
+        if (b >= dyn_batch) return;                         // no work left (uniform)
+        // wave-uniform values kept in scalar registers
+        chunk = __builtin_amdgcn_readfirstlane(chunk);
+        s = __builtin_amdgcn_readfirstlane(item - (__shfl(incl, b) - __shfl(n, b)));
+        T_dyn = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(t_lane, b));   // T < 2^31
+        if (b != b_early) load_q(b);   // uniform
+    } else {
+        s = blockIdx.x;
+        b = blockIdx.y;
+        chunk = chunk_arg;
+    }
     const int64_t c0 = (int64_t)s * chunk;   // < seq_cap: the grid has ceil(seq_cap / chunk) chunks
     // until the sequence length arrives, tiles are bounded by the cache capacity
-    int64_t cend = (c0 + chunk < seq_cap) ? c0 + chunk : seq_cap;
+    // (the device-side split knows it already)
+    const int64_t cap_b = dyn_batch > 0 ? T_dyn : seq_cap;
+    int64_t cend = (c0 + chunk < cap_b) ? c0 + chunk : cap_b;
     const int t = lane & 31, hh = lane >> 5;
     const uint8_t *seq = codes + (size_t)b * seq_cap * P;
     // the sequence length is requested first and used once Q~ is in LDS
-    const int32_t T_raw = seq_lens[b];
+    const int32_t T_raw = dyn_batch > 0 ? (int32_t)T_dyn : seq_lens[b];
     uint8_t *ring = ring_lds + wave * D * SLOTB;
     uint8_t *tile = tile_lds + wave * 32 * TS;
 
@@ -816,17 +900,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         }
         cend = (c0 + chunk < T) ? c0 + chunk : T;
     } else {
-        constexpr int QROW = GP + 8;
         _Float16 *qsm = reinterpret_cast<_Float16 *>(tile_lds);   // the tiles are free here
-        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
-        constexpr int NQ16 = 32 * GP / 8;
-        constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
-        u32x4 qreg[NQI];
-#pragma unroll
-        for (int u = 0; u < NQI; ++u) {
-            const int i = threadIdx.x + u * NW * 64;
-            qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
-        }
 #pragma unroll
         for (int u = 0; u < NQI; ++u) {
             // threads past the last chunk rewrite it with the same data (no
@@ -1132,7 +1206,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
-    int chunk, int S, int natural, int bits) {
+    int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta) {
     using VT = typename VecT<VW>::T;
     // W_v vectors per thread: a row is shared by TPR >= 4 threads (d_h <= 256),
     // so at most NVA per thread; NVT of them (at most 32 VGPRs) are held from the
@@ -1152,6 +1226,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     // splits of the workspace (indices clamped) before it arrives, and entries
     // of splits at or past the sequence's split count ns are discarded by selects.
     const int32_t T_raw = seq_lens[b];
+    // device-side split: every length, one per lane, ahead of the W_v loads so
+    // that waiting for them does not wait for W_v
+    const int32_t tl_raw = dyn_batch > 1 && (tid & 63) < dyn_batch ? seq_lens[tid & 63] : 0;
     // ---- issue: W_v row d, vectors part, part + TPR, ... (first: W_v is the
     // coldest data, read from HBM, while the partials were just written)
     const int g = h / (n_q / n_kv);
@@ -1168,6 +1245,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
         const int vi = part + TPR * i;
         if (vi < NV) wv[i] = wrow[vi];   // others unused
     }
+    // the chunk of the split kernel: the plan's, or the device-side split's (which
+    // also bounds the rows worth reading: the sequence's split count)
+    int chunk = chunk_arg, s_rows = S;
+    if (dyn_batch > 0) {
+        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
+        const int64_t tl = tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
+        const int nsb = (int)((tb + chunk - 1) / chunk);
+        s_rows = nsb < 1 ? 1 : nsb;
+    }
     // ---- issue: partial rows sg + u SG and their (m, l)
     const int KG = GP / 8, SG = kMergeThreads / KG;
     // level 2 uses TPP threads per position; zpart rows are padded to ZS floats,
@@ -1182,7 +1269,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     float2 mr[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        const int i = sg + u * SG, ic = zthr && i < S ? i : 0;
+        const int i = sg + u * SG, ic = zthr && i < s_rows ? i : 0;
         v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)ic * srow * GP);
         mr[u] = ml[(size_t)ic * srow];
     }
@@ -1312,7 +1399,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
 static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint16_t *W_kv,
                                const int32_t *seq_lens, uint16_t *out, int64_t seq_cap, int G,
                                int GP, int n_q, int n_kv, int d_h, int batch, int chunk, int S,
-                               int natural, int bits, hipStream_t st) {
+                               int natural, int bits, int dyn_batch, int ncta, hipStream_t st) {
     if (S < 1 || S > kMergeMaxS || GP > kMaxG || d_h > kMaxDh) return hipErrorInvalidValue;
     const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
                    : ((G & 3) == 0 && ((uintptr_t)W_kv & 7) == 0) ? 4
@@ -1330,7 +1417,7 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
     if (vw == VWX && r == RX) {                                                                           \
         decode_merge_kernel<VWX, RX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out, seq_cap, \
                                                                    G, GP, n_q, n_kv, d_h, chunk, S,       \
-                                                                   natural, bits);                        \
+                                                                   natural, bits, dyn_batch, ncta);       \
         return hipGetLastError();                                                                         \
     }
 #define FSQ_MERGE_VW(VWX) FSQ_MERGE_CASE(VWX, 2) FSQ_MERGE_CASE(VWX, 4) FSQ_MERGE_CASE(VWX, 8)
@@ -1370,8 +1457,11 @@ static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, cons
                                   int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
     constexpr int NW = kStreamWaves;
-    dim3 grid(pl.S, batch, pl.nqp / 32);
+    // device-side split: ncta + batch CTAs cover every work item (the per-sequence
+    // rounding up adds at most one item per sequence)
+    dim3 grid(pl.dyn ? pl.ncta + batch : pl.S, pl.dyn ? 1 : batch, pl.nqp / 32);
     dim3 block(NW * 64);
+    const int dyn_batch = pl.dyn ? batch : 0;
     // 16-byte row reads when every token row starts on a 16-byte boundary and a
     // lane half is whole 16-byte chunks
     constexpr bool kCanAl = GP % 64 == 0;
@@ -1380,10 +1470,10 @@ static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, cons
     const ReconArgs ra{};
     if (ev0 && ev1)
         hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
-                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S, ra);
+                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S, dyn_batch, pl.ncta, ra);
     else
         k<<<grid, block, 0, st>>>(qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, pl.nqp, pl.chunk,
-                                  pl.S, ra);
+                                  pl.S, dyn_batch, pl.ncta, ra);
     return hipGetLastError();
 }
 
@@ -1401,7 +1491,7 @@ static hipError_t launch_recon(int chunk, int S, const uint8_t *codes, const int
     constexpr bool kCanAl = GP % 64 == 0;
     const bool al = kCanAl && G == GP && ((uintptr_t)codes & 15) == 0;
     auto k = al ? decode_stream_kernel<GP, NW, D, kCanAl, RC> : decode_stream_kernel<GP, NW, D, false, RC>;
-    k<<<grid, block, 0, st>>>(nullptr, codes, seq_lens, pz, pml, seq_cap, G, n_q, 0, chunk, S, ra);
+    k<<<grid, block, 0, st>>>(nullptr, codes, seq_lens, pz, pml, seq_cap, G, n_q, 0, chunk, S, 0, 0, ra);
     return hipGetLastError();
 }
 
@@ -1498,7 +1588,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         if (e != hipSuccess) return e;
     }
     return launch_merge(pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, batch, pl.chunk,
-                        pl.S > 0 ? pl.S : 1, pl.stream, bits, st);
+                        pl.S > 0 ? pl.S : 1, pl.stream, bits, pl.dyn ? batch : 0, pl.ncta, st);
 }
 
 // The key-reconstruction comparison: no absorption launch; the split kernel
@@ -1559,7 +1649,7 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
     }
     const int chunk_i = S > 0 ? (int)chunk : pl.chunk;
     return launch_merge(pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, batch, chunk_i,
-                        S > 0 ? S : 1, 1, 4, st);
+                        S > 0 ? S : 1, 1, 4, 0, 0, st);
 }
 
 }  // namespace fsq

@@ -24,6 +24,12 @@ inline int split_waves(int GP) { return GP >= 128 ? 8 : 4; }
 // tokens.
 constexpr int kStreamWaves = 4;
 constexpr int kStreamMinTiles = 4;
+// Streaming calls of up to kDynMaxBatch sequences split on the device from the
+// actual lengths (one lane per sequence there); the chunk is then at least
+// kStreamMinTiles rounds and at least seq_cap / kDynMaxSplits, which bounds a
+// sequence's split count for the workspace.
+constexpr int kDynMaxBatch = 64;
+constexpr int kDynMaxSplits = 1024;
 inline int stream_depth(int GP) { return GP >= 128 ? 3 : 4; }
 inline int stream_target(int GP) { return GP >= 128 ? 512 : 768; }
 
@@ -34,6 +40,9 @@ struct DecodePlan {
     int S = 0;        // splits per sequence (0 when seq_cap == 0)
     int waves = 0;    // waves per split-K CTA
     int stream = 0;   // 1: decode_stream_kernel (partials in natural coordinate order)
+    int dyn = 0;      // 1: streaming with the device-side split; chunk and S are then
+                      // the smallest chunk and the largest split count per sequence
+    int ncta = 0;     // dyn: CTAs the tokens of all sequences are spread over
     size_t off_qt = 0, off_acc = 0, off_ml = 0, total = 0;
 };
 
@@ -57,6 +66,13 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     int64_t per = (work + target - 1) / target;
     if (per < quantum) per = quantum;
     per = (per + quantum - 1) / quantum * quantum;
+    if (p.stream && batch <= kDynMaxBatch) {
+        p.dyn = 1;
+        p.ncta = starget;
+        int64_t cmin = (seq_cap + kDynMaxSplits - 1) / kDynMaxSplits;
+        if (cmin < (int64_t)kStreamMinTiles * squant) cmin = (int64_t)kStreamMinTiles * squant;
+        per = (cmin + squant - 1) / squant * squant;
+    }
     if (per > (int64_t)1 << 30) per = (int64_t)1 << 30;
     p.chunk = (int)per;
     p.S = (int)((seq_cap + p.chunk - 1) / p.chunk);

@@ -107,8 +107,10 @@ size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t
 /*
  * fsq_decode_plan_info - how fsq_decode_attn (4-bit codes) splits a call of
  * these sizes: *kernel = 0 for the round-synchronous split-K kernel (short
- * chunks), 1 for the streaming split-K kernel (long chunks); *splits = chunks
- * per sequence; *chunk = tokens per chunk. Host arithmetic only.
+ * chunks), 1 for the streaming split-K kernel (long chunks), 2 for the
+ * streaming kernel with the split chosen on the device from the actual
+ * lengths (batches of up to 64 sequences); *splits = chunks per sequence (2: at
+ * most); *chunk = tokens per chunk (2: at least). Host arithmetic only.
  * Errors: FSQ_ERR_SHAPE (invalid sizes), FSQ_ERR_NULL (an output pointer NULL).
  */
 int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap, int32_t *kernel,

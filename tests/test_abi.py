@@ -195,10 +195,21 @@ def test_decode_plan_host_logic():
     assert fsq.decode_plan(1, 32, 84, 131072)["kernel"] == "decode_split_kernel"
     assert fsq.decode_plan(1, 32, 84, 1 << 20)["kernel"] == "decode_stream_kernel"
     assert fsq.decode_plan(16, 16, 256, 65536)["kernel"] == "decode_stream_kernel"
-    for args in [(1, 32, 256, 1), (1, 32, 84, 1 << 20), (16, 16, 256, 65536), (3, 12, 37, 5000)]:
+    for args in [(1, 32, 256, 1), (1, 32, 84, 1 << 20), (16, 16, 256, 65536), (3, 12, 37, 5000),
+                 (65, 16, 256, 65536)]:
         p = fsq.decode_plan(*args)
         assert p["splits"] * p["chunk"] >= args[3] > (p["splits"] - 1) * p["chunk"]
         assert p["splits"] <= 1024 and p["chunk"] % 128 == 0
+    # streaming calls of up to 64 sequences split on the device from the actual
+    # lengths: the plan then gives the smallest chunk (4 rounds of 4 waves x 32
+    # tokens, and at least seq_cap / 1024) and the largest split count
+    p = fsq.decode_plan(16, 16, 256, 65536)
+    assert p["device_split"] and p["chunk"] == 512 and p["splits"] == 128
+    p = fsq.decode_plan(1, 32, 84, 1 << 20)
+    assert p["device_split"] and p["chunk"] == 1024 and p["splits"] == 1024
+    assert not fsq.decode_plan(65, 16, 256, 65536)["device_split"]
+    assert fsq.decode_plan(65, 16, 256, 65536)["kernel"] == "decode_stream_kernel"
+    assert not fsq.decode_plan(1, 32, 256, 32768)["device_split"]
     assert fsq.decode_plan(1, 32, 256, 0)["splits"] == 0
     with pytest.raises(fsq.FsqError):
         fsq.decode_plan(0, 32, 256, 10)

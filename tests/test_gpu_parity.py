@@ -217,6 +217,35 @@ def test_decode_stream_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
             assert e < REL_L2, (b, e)
 
 
+# The device-side split of streaming calls (up to 64 sequences): the chunk
+# comes from the sum of the actual lengths, and consecutive work items cover
+# the sequences in order, so very uneven batches, empty sequences, a length far
+# below the capacity, the 64-sequence limit and the static split just past it
+# (65 sequences) all take different item layouts.
+@pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens", [
+    (64, 8, 2, 64, 32, 8192, "skew"),
+    (65, 8, 2, 64, 32, 8192, "skew"),
+    (8, 16, 8, 128, 84, 65536, [0, 0, 60000, 3, 0, 129, 0, 5]),
+    (1, 32, 8, 128, 84, 1 << 20, [300001]),
+    (6, 16, 4, 128, 256, 65536, [1, 2, 3, 4, 5, 65536]),
+])
+def test_decode_stream_device_split_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
+    if lens == "skew":
+        g = synth.rng(201, B, 0)
+        lens = [int(x) for x in g.integers(0, 3000, size=B)]
+        lens[3], lens[10], lens[B - 1] = 0, 8192, 1
+    q, packed, W, lens = decode_case(G * 7 + cap + B, B, n_q, n_kv, d_h, G, cap, lens)
+    assert fsq.decode_plan(B, n_q, G, cap)["kernel"] == "decode_stream_kernel"
+    got = run_decode(fsq, q, packed, W, lens, n_kv)
+    ref = oracle_decode(q, packed, W, lens, n_kv, G)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0)
+        else:
+            e = rel_l2(got[b], ref[b])
+            assert e < REL_L2, (b, e)
+
+
 def test_decode_stream_deterministic(fsq):
     q, packed, W, lens = decode_case(8, 4, 32, 8, 128, 84, 65536, [30000, 17, 65536, 4100])
     a = run_decode(fsq, q, packed, W, lens, 8)
