@@ -186,26 +186,28 @@ def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
 
 
 # Caches whose capacity (batch x seq_cap) is large enough for the streaming
-# split-K kernel (every wave gets several 32-token tiles; 131072 tokens at
-# G > 96, 262144 below), with lengths mostly far shorter than the capacity so
-# the oracle stays cheap: empty and one-token sequences, tails inside a tile,
-# sequences spanning several chunks, odd capacities (rows of a sequence not
-# 16-byte aligned), odd G, every pooling block count 1..8, and two head groups.
+# split-K kernel (every wave gets at least 4 tiles of 32 tokens: more than
+# 196608 tokens at GP >= 128, 393216 below; the test checks the plan), with
+# lengths mostly far shorter than the capacity so the oracle stays cheap: empty
+# and one-token sequences, tails inside a tile, sequences spanning several
+# chunks, odd capacities (rows of a sequence not 16-byte aligned), odd G, every
+# pooling block count 1..8, and two head groups.
 @pytest.mark.parametrize("B,n_q,n_kv,d_h,G,cap,lens", [
-    (2, 32, 8, 128, 256, 65536, [3000, 1]),
-    (2, 32, 8, 128, 256, 65536, [20000, 4097]),
-    (4, 32, 8, 128, 84, 65536, [0, 5000, 700, 12345]),
-    (4, 32, 8, 128, 84, 65537, [65537, 1, 31, 33]),
-    (4, 16, 8, 128, 64, 65536, [1000, 65536, 0, 2]),
-    (4, 8, 1, 64, 37, 65536, [3001, 129, 1, 64]),
-    (2, 40, 8, 128, 200, 65536, [7000, 333]),
-    (2, 32, 8, 128, 160, 65536, [9999, 65536]),
-    (2, 32, 4, 128, 128, 65536, [4096, 100]),
-    (4, 32, 8, 128, 32, 65536, [2000, 1, 0, 513]),
-    (4, 64, 8, 128, 96, 65536, [1500, 4000, 10, 600]),
-    (3, 16, 8, 128, 256, 65521, [65521, 40000, 77]),
+    (2, 32, 8, 128, 256, 131072, [3000, 1]),
+    (2, 32, 8, 128, 256, 131072, [20000, 4097]),
+    (4, 32, 8, 128, 84, 131072, [0, 5000, 700, 12345]),
+    (4, 32, 8, 128, 84, 131073, [65537, 1, 31, 33]),
+    (4, 16, 8, 128, 64, 131072, [1000, 65536, 0, 2]),
+    (4, 8, 1, 64, 37, 131072, [3001, 129, 1, 64]),
+    (2, 40, 8, 128, 200, 131072, [7000, 333]),
+    (2, 32, 8, 128, 160, 131072, [9999, 65536]),
+    (2, 32, 4, 128, 128, 131072, [4096, 100]),
+    (4, 32, 8, 128, 32, 131072, [2000, 1, 0, 513]),
+    (4, 64, 8, 128, 96, 131072, [1500, 4000, 10, 600]),
+    (3, 16, 8, 128, 256, 131071, [65521, 40000, 77]),
 ])
 def test_decode_stream_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
+    assert fsq.decode_plan(B, n_q, G, cap)["kernel"] == "decode_stream_kernel"
     q, packed, W, lens = decode_case(G * 13 + cap, B, n_q, n_kv, d_h, G, cap, lens)
     got = run_decode(fsq, q, packed, W, lens, n_kv)
     ref = oracle_decode(q, packed, W, lens, n_kv, G)
@@ -247,7 +249,8 @@ def test_decode_stream_device_split_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens)
 
 
 def test_decode_stream_deterministic(fsq):
-    q, packed, W, lens = decode_case(8, 4, 32, 8, 128, 84, 65536, [30000, 17, 65536, 4100])
+    assert fsq.decode_plan(4, 32, 84, 131072)["kernel"] == "decode_stream_kernel"
+    q, packed, W, lens = decode_case(8, 4, 32, 8, 128, 84, 131072, [30000, 17, 65536, 4100])
     a = run_decode(fsq, q, packed, W, lens, 8)
     b = run_decode(fsq, q, packed, W, lens, 8)
     assert np.array_equal(a, b)
