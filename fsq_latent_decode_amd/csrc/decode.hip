@@ -30,6 +30,19 @@ namespace fsq {
 
 constexpr int kTile = 32;        // tokens per wave and round (the score MFMA's M)
 
+// Lane l's value combined with lane l ^ 32's through v_permlane32_swap (a VALU
+// exchange of the wave's halves; a shuffle would go through the LDS crossbar).
+// The swap returns the pair in an order that is the same for both lanes, so
+// both compute the same bits.
+__device__ inline float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Codes of one packed dword (8 codes, nibble i = coordinate 8D + i) as fp16
 // operands in the order (c0,c4)(c1,c5)(c2,c6)(c3,c7). The bit pattern n of a
 // code is the fp16 subnormal n * 2^-24, exact, so no bias is subtracted here:
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             sv[r] = tok < ntok ? sc[r] : -INFINITY;
             tmax = fmaxf(tmax, sv[r]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kCodeScale;
+        tmax = halves_max(tmax) * kCodeScale;
         if (lane < 32) tmax_s[wave][t] = tmax;
         __syncthreads();
 
@@ -443,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             p[r] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[r], kCodeScale, -m_new));
             psum += (float)p[r];   // the normaliser sums the fp16 weights the pooling uses
         }
-        psum += __shfl_xor(psum, 32);
+        psum = halves_sum(psum);
         if (lane < 32) tsum_s[wave][t] = psum;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -1016,7 +1029,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) ss = fmaf(kt[db][r], kt[db][r], ss);
-                ss += __shfl_xor(ss, 32);
+                ss = halves_sum(ss);
                 const float inv = __builtin_amdgcn_rsqf(ss / (float)ra.d_h + ra.eps);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
@@ -1076,7 +1089,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * kSS;
+        tmax = halves_max(tmax) * kSS;
         const bool bump = tmax > m_ref + kRescaleSlack;
         const float m_new = bump ? tmax : m_ref;
         const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
@@ -1120,7 +1133,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // zbar = 2^24 sum c_w acc_w / L - 8, summed in wave order
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // prologue loads past the length may be in flight
     lds_barrier();                          // every wave is done with its ring and tile
-    const float l_w = l_run + __shfl_xor(l_run, 32);
+    const float l_w = halves_sum(l_run);
     if (lane < 32) {
         ms[wave][lane] = m_ref;
         ls[wave][lane] = l_w;
