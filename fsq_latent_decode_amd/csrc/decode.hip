@@ -22,6 +22,8 @@
 //                       chunks' zbar, then out = W_v,g zbar
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "append_gemv.h"
 #include "common.h"
 #include "decode_plan.h"
@@ -603,7 +605,8 @@ struct StreamCfg {
     static constexpr int SLOTB = NEED < 1024 ? 1024 : (NEED + 127) / 128 * 128;
     static constexpr int NI = (SLOTB + 1023) / 1024;   // direct-to-LDS loads per tile (64 lanes x 16 B)
     static constexpr int RING = NW * D * SLOTB;
-    static constexpr int TILE = NW * 32 * TS;
+    static constexpr bool PAIR = GP < 128;             // tiles taken two at a time (absorbed queries)
+    static constexpr int TILE = NW * 32 * TS * (PAIR ? 2 : 1);   // per-wave nibble tile(s)
     static constexpr int QST = 32 * (GP + 8) * 2;      // Q~ staging, prologue only (aliases the tiles)
     static constexpr int CBYTES = NW * 64 * 16 * 4;    // one coordinate block of every wave's sums
     static constexpr int BPP0 = RING / CBYTES;
@@ -731,7 +734,7 @@ __device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int 
 }
 
 template <int GP, int NW, int D, bool AL, int RC>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 4)))) void decode_stream_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 3)))) void decode_stream_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
     float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk_arg, int S,
@@ -825,7 +828,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // the sequence length is requested first and used once Q~ is in LDS
     const int32_t T_raw = dyn_batch > 0 ? (int32_t)T_dyn : seq_lens[b];
     uint8_t *ring = ring_lds + wave * D * SLOTB;
-    uint8_t *tile = tile_lds + wave * 32 * TS;
+    uint8_t *tile = tile_lds + wave * 32 * TS * (C::PAIR ? 2 : 1);
 
     auto tiles_before = [&](int64_t e) -> int {   // this wave's tiles starting before token e
         const int64_t first = c0 + (int64_t)kTile * wave;
@@ -952,6 +955,130 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     const uint32_t tr_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)trsrc;
     uint8_t *tdst = tile + tile_row(t) * TS + hh * (GP / 4);
 
+    if constexpr (C::PAIR && !RC) {
+        // Two tiles per step: two independent score chains, one softmax update
+        // (max, rescale) for 64 tokens, and pooling from two nibble tiles, which
+        // gives a wave twice the independent work between its waits. Tiles j and
+        // j + 1 sit in slots j % D and (j + 1) % D; this step refills the slots
+        // the previous step emptied, keeping D - 2 tiles in flight beyond it.
+        constexpr int kWaitPair = (((D - 2) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 2) * NI) >> 4) << 14);
+        auto step = [&](auto ntl_c, int j) {
+            constexpr int NTL = decltype(ntl_c)::value;
+            uint32_t cur[NTL][KB];
+            int ntok[NTL];
+#pragma unroll
+            for (int u = 0; u < NTL; ++u) {
+                const int64_t t0 = tile_t0(j + u);
+                const int64_t rem = cend - t0;
+                ntok[u] = rem < kTile ? (int)rem : kTile;
+                const uint8_t *slot = ring + ((j + u) % D) * SLOTB;
+                if (AL) {
+#pragma unroll
+                    for (int i = 0; i < KB / 4; ++i) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + slot_phys(t * P + hh * (GP / 4) + 16 * i));
+                        cur[u][4 * i + 0] = v.x;
+                        cur[u][4 * i + 1] = v.y;
+                        cur[u][4 * i + 2] = v.z;
+                        cur[u][4 * i + 3] = v.w;
+                    }
+                } else {
+                    const int mis = (int)((uintptr_t)(seq + (size_t)t0 * P) & 15);
+                    const int a = mis + t * P + hh * (GP / 4);
+                    const int a0 = a & ~3, sh = (a & 3) * 8;
+                    uint32_t ld[KB + 1];
+#pragma unroll
+                    for (int i = 0; i < KB + 1; ++i) ld[i] = *reinterpret_cast<const uint32_t *>(slot + slot_phys(a0 + 4 * i));
+#pragma unroll
+                    for (int i = 0; i < KB; ++i) cur[u][i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
+                }
+#pragma unroll
+                for (int i = 0; i < KB / 2; ++i)
+                    *reinterpret_cast<uint2 *>(tdst + u * 32 * TS + 8 * i) = uint2{cur[u][2 * i], cur[u][2 * i + 1]};
+            }
+            // scores, the tiles' chains interleaved
+            floatx16 sc[NTL];
+#pragma unroll
+            for (int u = 0; u < NTL; ++u) sc[u] = floatx16{};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int u = 0; u < NTL; ++u)
+                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[u][kb]), qv[kb], sc[u], 0, 0, 0);
+            // online softmax over the step's tokens (lane: head t, tokens tok(r))
+            float sv[NTL][16];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < NTL; ++u) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sv[u][r] = sc[u][r];
+                if (ntok[u] < kTile) {   // the chunk's last tile only (uniform)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int tok = (r >> 2) * 8 + hh * 4 + (r & 3);
+                        sv[u][r] = tok < ntok[u] ? sv[u][r] : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[u][r]);
+            }
+            tmax = halves_max(tmax) * kSS;
+            const bool bump = tmax > m_ref + kRescaleSlack;
+            const float m_new = bump ? tmax : m_ref;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+            const bool rescale = bump && m_ref != -INFINITY;
+            m_ref = m_new;
+            half2 ph[NTL][8];
+            float psum = 0.0f;
+            const half2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int u = 0; u < NTL; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[u][2 * i], kSS, -m_new));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[u][2 * i + 1], kSS, -m_new));
+                    ph[u][i] = half2{(_Float16)e0, (_Float16)e1};
+                    psum = __builtin_amdgcn_fdot2(ph[u][i], one2, psum, false);
+                }
+            l_run = l_run * alpha + psum;
+            if (__any(rescale)) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+            }
+            // pooling (B operands as in the one-tile loop below)
+            const half2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+            v2i32 zt[NTL][CB];
+#pragma unroll
+            for (int u = 0; u < NTL; ++u) tr4_reads<CB>(tr_addr + u * 32 * TS, zt[u]);
+#pragma unroll
+            for (int u = 0; u < NTL; ++u) {
+                const half2 q1 = ph[u][1] * s16, q3 = ph[u][3] * s16, q5 = ph[u][5] * s16, q7 = ph[u][7] * s16;
+                const half8 pv0 = {ph[u][0].x, ph[u][0].y, q1.x, q1.y, ph[u][2].x, ph[u][2].y, q3.x, q3.y};
+                const half8 pv1 = {ph[u][4].x, ph[u][4].y, q5.x, q5.y, ph[u][6].x, ph[u][6].y, q7.x, q7.y};
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zt[u][cb][0]), pv0, acc[cb], 0, 0, 0);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zt[u][cb][1]), pv1, acc[cb], 0, 0, 0);
+                }
+            }
+        };
+        int j = 0;
+        for (; j + 1 < nt; j += 2) {
+            // refill the slots of tiles j - 2 and j - 1 (at j = 0: slot D - 1,
+            // the one the prologue left free)
+            const int lo = j + D - 2 > D - 1 ? j + D - 2 : D - 1;
+            for (int k = lo; k <= j + D - 1; ++k)
+                if (k < nt) issue(k);
+            if (j + D <= nt)   // tiles j + 2 .. j + D - 1 may stay in flight
+                __builtin_amdgcn_s_waitcnt(kWaitPair);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitAll);
+            step(std::integral_constant<int, 2>{}, j);
+        }
+        if (j < nt) {   // an odd last tile
+            __builtin_amdgcn_s_waitcnt(kWaitAll);
+            step(std::integral_constant<int, 1>{}, j);
+        }
+    } else
     for (int j = 0; j < nt; ++j) {
         const bool ahead = j + D - 1 < nt;
         if (ahead) issue(j + D - 1);   // into the slot tile j - 1 used

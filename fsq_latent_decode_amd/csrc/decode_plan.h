@@ -31,7 +31,7 @@ constexpr int kStreamMinTiles = 4;
 constexpr int kDynMaxBatch = 64;
 constexpr int kDynMaxSplits = 1024;
 inline int stream_depth(int GP) { return GP >= 128 ? 3 : 4; }
-inline int stream_target(int GP) { return GP >= 128 ? 512 : 1024; }
+inline int stream_target(int GP) { return GP >= 128 ? 512 : 768; }
 
 struct DecodePlan {
     int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
