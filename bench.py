@@ -610,10 +610,12 @@ def summarize(w, ms, call_ms, replicas):
         avg = float(np.mean(call_ms))
         nbytes = split_kernel_bytes(w, lens)
         ach = nbytes / (avg * 1e-3) / 1e9
+        split = ({"split": "on the device from the lengths", "splits_per_sequence_max": plan["splits"],
+                  "chunk_tokens_min": plan["chunk"]} if plan["device_split"] else
+                 {"split": "host plan", "splits_per_sequence": plan["splits"], "chunk_tokens": plan["chunk"]})
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic_from_profile(w),
-                           "kernel": plan["kernel"], "splits_per_sequence": plan["splits"],
-                           "chunk_tokens": plan["chunk"], "bytes_per_launch": nbytes,
+                           "kernel": plan["kernel"], **split, "bytes_per_launch": nbytes,
                            "avg_launch_us": avg * 1e3, "launches_timed": len(call_ms),
                            "timing": "hipExtLaunchKernelGGL start/stop events, eager steps"}
     return res
