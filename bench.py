@@ -324,13 +324,15 @@ def cpu_baseline(w, seconds, gpu_out=None):
         return orc.decode_attn(q, packed, Wf, lens, w.n_kv, w.G)
 
     def run(budget, keep):
+        # layers in order, wrapping to further steps until the time budget is
+        # spent (the inputs of a layer are the same in every step)
         done, t_total, outs = 0, 0.0, {}
-        while t_total < budget and done < w.layers:
-            args = inputs(done)
+        while t_total < budget:
+            args = inputs(done % w.layers)
             t = time.perf_counter()
             out = layer(*args)
             t_total += time.perf_counter() - t
-            if keep:
+            if keep and done < w.layers:
                 outs[done] = out
             done += 1
         return done, t_total, outs
@@ -339,8 +341,8 @@ def cpu_baseline(w, seconds, gpu_out=None):
     per_step = t_total / done * w.layers
     res = {"value": float(np.sum(lens)) / per_step, "unit": "context-tokens/s", "cores": threads,
            "kind": "oracle",
-           "sample": f"{done} of {w.layers} layers (one-token append + decode at full context), "
-                     f"{t_total:.1f} s, extrapolated x{w.layers / done:.1f} to one step",
+           "sample": f"{done} layers ({done / w.layers:.2f} steps of {w.layers} layers; one-token append + "
+                     f"decode at full context), {t_total:.1f} s of oracle time, scaled to one step",
            "step_s": per_step, "cpu_count": os.cpu_count(),
            "affinity_cores": len(os.sched_getaffinity(0))}
     if threadpool_limits is not None:
