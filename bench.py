@@ -220,6 +220,17 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
 
+    # phase A2: the same steps again, one event pair per step, for the spread
+    per = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run(warmup + steps + i)
+        b.record()
+        per.append((a, b))
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in per]
+
     # phase B: eager steps with HIP events around every split-K kernel launch
     call_ms = []
     for i in range(timing_steps if w.levels == 16 else 0):   # the event-timed entry point is 4-bit only
@@ -228,7 +239,16 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
         m.step((warmup + steps + i) % replicas, ev)
         torch.cuda.synchronize()
         call_ms.extend(a.elapsed_time(b) for a, b in ev)
-    return m, ms, call_ms, replicas
+    return m, ms, call_ms, replicas, step_ms
+
+
+def step_spread(step_ms, seed=0, resamples=2000):
+    """Median of per-step times with a 95% bootstrap interval of the median."""
+    x = np.asarray(step_ms, dtype=np.float64)
+    g = np.random.default_rng(seed)
+    med = np.median(g.choice(x, size=(resamples, x.size), replace=True), axis=1)
+    return {"median_ms": float(np.median(x)), "ci95_ms": [float(np.percentile(med, 2.5)), float(np.percentile(med, 97.5))],
+            "steps": int(x.size), "timing": "one event pair per graph-replayed step"}
 
 
 def append_prefill(w, torch, calls=40, eager=False):
@@ -640,18 +660,20 @@ def main():
                                         eager=args.eager)))
         return
     w = synth.WORKLOADS[args.workload]
-    m, ms, call_ms, reps = run_workload(w, torch, args.steps, args.warmup, args.eager,
-                                        args.timing_steps, args.two_call)
+    m, ms, call_ms, reps, step_ms = run_workload(w, torch, args.steps, args.warmup, args.eager,
+                                                 args.timing_steps, args.two_call)
     main_res = summarize(w, ms, call_ms, reps)
+    main_res["step_spread"] = step_spread(step_ms)
     gpu_out = {l: d["out"].float().cpu().numpy().astype(np.float64) for l, d in enumerate(m.reps[0])}
     del m
     torch.cuda.empty_cache()
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
         w2 = synth.WORKLOADS[name]
-        m2, ms2, cm2, reps2 = run_workload(w2, torch, max(5, args.steps // 2), args.warmup,
-                                           args.eager, args.timing_steps, args.two_call)
+        m2, ms2, cm2, reps2, sm2 = run_workload(w2, torch, max(5, args.steps // 2), args.warmup,
+                                                args.eager, args.timing_steps, args.two_call)
         also[name] = summarize(w2, ms2, cm2, reps2)
+        also[name]["step_spread"] = step_spread(sm2)
         del m2
         torch.cuda.empty_cache()
     sdpa = {}
@@ -698,6 +720,7 @@ def main():
                             else "per layer: fsq_decode_step (append of the new token + attention)")},
         "decode_steps_per_s": main_res["steps_per_s"],
         "step_roofline": main_res["step_roofline"],
+        "step_spread": main_res["step_spread"],
         "roofline": main_res.get("roofline"),
         "cpu_baseline": cpu,
         "also": also,
