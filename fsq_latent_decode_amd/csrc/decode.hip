@@ -17,8 +17,10 @@
 //                       codes -> registers (prefetched one round ahead) -> fp16
 //                       operands -> MFMA scores (all heads share z) -> LDS tile
 //                       -> online softmax (exp2) -> MFMA latent pooling ->
-//                       (m, l, zbar fp16)
-//   decode_merge_kernel one CTA per (sequence, head): log-sum-exp merge of the
+//                       (m, l, zbar fp16); for long chunks decode_stream_kernel
+//                       (below) instead, split on the device for batches
+//   decode_merge_kernel one 16-wave CTA per (sequence, head) (or up to four
+//                       sharing a head's W_v rows): log-sum-exp merge of the
 //                       chunks' zbar, then out = W_v,g zbar
 #include <hip/hip_ext.h>
 
