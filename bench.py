@@ -166,7 +166,7 @@ class Model:
                     T = int(self.lens_np[b])
                     fsq.fsq_append(d["x"][b:b + 1], d["E"], d["codes"][b, T - 1:T], levels=w.levels)
                 fsq.fsq_decode_attn_levels(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv, w.levels,
-                                           workspace=self.ws)
+                                           workspace=self.ws, split_events=None if ev is None else ev[l])
                 continue
             if ev is None and not two_call:
                 fsq.fsq_decode_step(d["x"], d["E"], d["q"], d["codes"], d["W"], self.lens, d["out"],
@@ -233,7 +233,7 @@ def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
 
     # phase B: eager steps with HIP events around every split-K kernel launch
     call_ms = []
-    for i in range(timing_steps if w.levels == 16 else 0):   # the event-timed entry point is 4-bit only
+    for i in range(timing_steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(w.layers)]
         m.step((warmup + steps + i) % replicas, ev)

@@ -16,7 +16,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
-           "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels", "fsq_decode_plan_info")
+           "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels",
+           "fsq_decode_attn_levels_timed", "fsq_decode_plan_info")
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.fsq_append_levels.restype = ctypes.c_int
         L.fsq_decode_attn_levels.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp, sz, vp]
         L.fsq_decode_attn_levels.restype = ctypes.c_int
+        L.fsq_decode_attn_levels_timed.argtypes = L.fsq_decode_attn_levels.argtypes + [vp, vp]
+        L.fsq_decode_attn_levels_timed.restype = ctypes.c_int
         f32 = ctypes.c_float
         L.fsq_decode_attn_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, f32,
                                            vp, sz, vp]
@@ -200,19 +203,24 @@ def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes
 
 def fsq_decode_attn_levels(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor,
                            seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int, levels: int,
-                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                           workspace: torch.Tensor | None = None, stream=None,
+                           split_events=None) -> torch.Tensor:
     """fsq_decode_attn over a cache of L = levels codes per coordinate (4, 16, 256):
-    codes [B, cap, ceil(G b/8)] uint8, z = code - L/2."""
+    codes [B, cap, ceil(G b/8)] uint8, z = code - L/2. With split_events the call
+    goes through fsq_decode_attn_levels_timed."""
     if levels not in LEVEL_BITS:
         raise ValueError(f"levels must be one of {sorted(LEVEL_BITS)}")
     B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels)
     if workspace is None:
         workspace = alloc_workspace(B, n_q, G, cap, q.device)
     _dev(workspace, "workspace", torch.uint8, 1)
-    rc = lib().fsq_decode_attn_levels(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(),
-                                      seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, levels,
-                                      cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
-    _check(rc, "fsq_decode_attn_levels")
+    args = (q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, n_q,
+            n_kv, d_h, G, levels, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if split_events is None:
+        _check(lib().fsq_decode_attn_levels(*args), "fsq_decode_attn_levels")
+    else:
+        ev = [_event_handle(e) for e in split_events]
+        _check(lib().fsq_decode_attn_levels_timed(*args, ev[0], ev[1]), "fsq_decode_attn_levels_timed")
     return out
 
 

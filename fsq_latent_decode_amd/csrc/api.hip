@@ -111,6 +111,17 @@ int fsq_decode_attn_levels(const uint16_t *q, const uint8_t *codes, const uint16
                          levels);
 }
 
+int fsq_decode_attn_levels_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                                 const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                                 int32_t n_kv, int32_t d_h, int32_t G, int32_t levels, int64_t seq_cap,
+                                 void *workspace, size_t workspace_bytes, void *stream, void *split_start,
+                                 void *split_stop) {
+    if (!split_start || !split_stop) return FSQ_ERR_NULL;
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                         workspace, workspace_bytes, stream, split_start, split_stop, nullptr, nullptr, 0,
+                         levels);
+}
+
 int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
                           const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
                           int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,

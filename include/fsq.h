@@ -183,6 +183,19 @@ int fsq_decode_attn_timed(const uint16_t *q, const uint8_t *codes, const uint16_
                           void *stream, void *split_start, void *split_stop);
 
 /*
+ * fsq_decode_attn_levels_timed - fsq_decode_attn_levels with the split-K kernel
+ * bracketed by two caller-created events, as fsq_decode_attn_timed (same
+ * results as fsq_decode_attn_levels; not for use under stream capture).
+ * Errors: as fsq_decode_attn_levels; FSQ_ERR_NULL if an event is NULL.
+ */
+int fsq_decode_attn_levels_timed(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                                 const int32_t *seq_lens, uint16_t *out,
+                                 int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                                 int32_t levels, int64_t seq_cap, void *workspace,
+                                 size_t workspace_bytes, void *stream, void *split_start,
+                                 void *split_stop);
+
+/*
  * fsq_decode_step - one decode step of one layer: append each sequence's new
  * token to its cache, then attend over the cache including that token.
  *

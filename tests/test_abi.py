@@ -181,6 +181,19 @@ def test_levels_validation_before_any_hip_call(levels, status):
 
 
 @needs_lib
+def test_timed_entry_points_need_both_events():
+    # the event-timed forms reject a NULL event before any HIP call
+    for ev in [(None, 256), (256, None)]:
+        assert fsq.lib().fsq_decode_attn_timed(256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 16, 256,
+                                               1 << 20, None, *ev) == fsq.FSQ_ERR_NULL
+        assert fsq.lib().fsq_decode_attn_levels_timed(256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 4, 16,
+                                                      256, 1 << 20, None, *ev) == fsq.FSQ_ERR_NULL
+    # and otherwise validate as the untimed forms
+    assert fsq.lib().fsq_decode_attn_levels_timed(256, 256, 256, 256, 256, 1, 32, 8, 128, 256, 5, 16,
+                                                  256, 1 << 20, None, 256, 256) == fsq.FSQ_ERR_UNSUPPORTED
+
+
+@needs_lib
 def test_levels_workspace_is_the_default_one():
     # the 2- and 8-bit decode needs no more workspace than fsq_decode_workspace_bytes
     ok = fsq.lib().fsq_decode_attn_levels(256, 256, 256, 256, 256, 1, 32, 8, 128, 84, 4, 1 << 20, 256,

@@ -375,6 +375,31 @@ def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
             assert e < REL_L2, (b, e)
 
 
+@pytest.mark.parametrize("levels", [4, 16, 256])
+def test_timed_decode_is_bitwise_the_untimed_one(fsq, levels):
+    """The event-timed entry points give the untimed results bit for bit, and
+    their events bracket a positive duration."""
+    B, n_q, n_kv, d_h, G, cap = 2, 32, 8, 128, 84, 3000
+    g = synth.rng(211, levels, 0)
+    q = dev_bf16(synth.normal_bf16(g, (B, n_q, d_h)))
+    W = dev_bf16(synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G)))
+    codes = dev_u8(synth.uniform_code_bytes(g, (B, cap), G, orc.bits_of_levels(levels)))
+    lens = torch.tensor([3000, 1234], dtype=torch.int32, device="cuda")
+    outs = []
+    for timed in (False, True):
+        out = torch.empty((B, n_q, d_h), dtype=torch.bfloat16, device="cuda")
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+        if levels == 16:
+            fsq.fsq_decode_attn(q, codes, W, lens, out, n_kv, split_events=ev)
+        else:
+            fsq.fsq_decode_attn_levels(q, codes, W, lens, out, n_kv, levels, split_events=ev)
+        torch.cuda.synchronize()
+        if timed:
+            assert ev[0].elapsed_time(ev[1]) > 0
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("levels,G", [(4, 168), (256, 42)])
 def test_levels_append_then_decode_at_the_g84_byte_budget(fsq, levels, G):
     """42 bytes per token (the G = 84 budget) spent on 2- or 8-bit codes:
