@@ -228,6 +228,7 @@ def test_decode_stream_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     (64, 8, 2, 64, 32, 8192, "skew"),
     (65, 8, 2, 64, 32, 8192, "skew"),
     (8, 16, 8, 128, 84, 65536, [0, 0, 60000, 3, 0, 129, 0, 5]),
+    (8, 16, 8, 128, 84, 65536, [0] * 8),                 # nothing to attend to anywhere
     (1, 32, 8, 128, 84, 1 << 20, [300001]),
     (6, 16, 4, 128, 256, 65536, [1, 2, 3, 4, 5, 65536]),
 ])
