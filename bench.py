@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-recon", action="store_true",
                     help="skip the key-reconstruction comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-layer-batched", action="store_true",
+                    help="skip the layer-batched measurement (all layers' attention in one call)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
     ap.add_argument("--timing-steps", type=int, default=5,
                     help="eager steps whose split-K launches are bracketed by HIP events")
@@ -556,6 +558,80 @@ def _time_sdpa(torch, F, sdpa_kernel, backends, layers, form, steps, warmup):
     return res
 
 
+def layer_batched(w, torch, steps=10, warmup=3):
+    """Not the model's call pattern: the attention of all the workload's layers in
+    ONE fsq_decode_attn call, the layers' caches and queries taken as a batch of
+    sequences under layer 0's W_kv. It shows the decode kernels with the GPU
+    filled (the per-layer calls of a decode step are bound by launch and
+    dependent-load latency); the same bytes and flops per layer as the step.
+    Replicas exceed the Infinity Cache; graph-replayed; then eager calls with
+    events around the split-K kernel."""
+    import fsq_latent_decode_amd as fsq
+    if w.batch != 1 or w.levels != 16:
+        return None
+    L, T = w.layers, int(w.context)
+    lens_np = np.full(L, T, dtype=np.int32)
+    nbytes = L * T * w.P
+    replicas = min(4, max(2, math.ceil(4 * MALL_BYTES / nbytes)))
+    dev = "cuda"
+    _, W = synth.layer_weights(w, 0)
+    Wd = torch.from_numpy(np.ascontiguousarray(W).view(np.int16)).view(torch.bfloat16).to(dev)
+    qs = np.concatenate([synth.layer_query(w, l) for l in range(L)], axis=0)
+    q = torch.from_numpy(np.ascontiguousarray(qs).view(np.int16)).view(torch.bfloat16).to(dev)
+    lens = torch.from_numpy(lens_np).to(dev)
+    reps = []
+    for r in range(replicas):
+        g = torch.Generator(device=dev)
+        g.manual_seed(7_000_001 * w.wid + r)
+        codes = torch.randint(0, 256, (L, T, w.P), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+        reps.append((codes, torch.empty((L, w.n_q, w.d_h), dtype=torch.bfloat16, device=dev)))
+    ws = fsq.alloc_workspace(L, w.n_q, w.G, T, dev)
+    plan = fsq.decode_plan(L, w.n_q, w.G, T)
+    call = lambda r, ev=None: fsq.fsq_decode_attn(q, reps[r][0], Wd, lens, reps[r][1], w.n_kv, workspace=ws,
+                                                  split_events=ev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for r in range(replicas):
+            call(r)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(replicas):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            call(r)
+        graphs.append(gr)
+    for i in range(warmup):
+        graphs[i % replicas].replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[(warmup + i) % replicas].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ks = []
+    for i in range(5):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        call(i % replicas, ev)
+        torch.cuda.synchronize()
+        ks.append(ev[0].elapsed_time(ev[1]))
+    k_ms = float(np.mean(ks))
+    del reps, graphs, ws
+    torch.cuda.empty_cache()
+    return {"what": f"all {L} layers' attention in one call: {L} caches and queries as a batch under one W_kv "
+                    "(not the model's call pattern, which is one dependent call per layer)",
+            "ms_per_call": ms, "context_tokens_per_s": L * T / (ms * 1e-3),
+            "kernel": plan["kernel"], "device_split": plan["device_split"],
+            "split_kernel_us": k_ms * 1e3,
+            "roofline": {"bound": "hbm", "achieved": nbytes / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": nbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": nbytes},
+            "call_roofline_frac": (nbytes / (HBM_PEAK_GBS * 1e9)) / (ms * 1e-3)}
+
+
 def recon_comparison(w, torch, fsq_ms, steps=10, warmup=3, rope=False):
     """The decode step with keys rebuilt per tile (fsq_decode_attn_recon; with
     rope, fsq_decode_attn_rope: key RMS norm with a seeded gain, eps 1e-6, and
@@ -694,6 +770,12 @@ def main():
             r = recon_comparison(w2, torch, fsq_ms[name], rope=True)
             if r is not None:
                 recon[name + "_rope"] = r
+    batched = {}
+    if not args.no_layer_batched:
+        for name in [n for n in [args.workload] + [s for s in args.also.split(",") if s] if n in COMPARED]:
+            r = layer_batched(synth.WORKLOADS[name], torch)
+            if r is not None:
+                batched[name] = r
     app = None
     for name in [args.workload] + [s for s in args.also.split(",") if s]:
         if synth.WORKLOADS[name].append_tokens and not args.no_append:
@@ -727,6 +809,7 @@ def main():
         "append_prefill": app,
         "sdpa_comparison": sdpa,
         "recon_comparison": recon,
+        "layer_batched": batched,
     }
     print(json.dumps(line))
 
