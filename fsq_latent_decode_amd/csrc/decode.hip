@@ -853,11 +853,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         const uintptr_t a0 = A & ~(uintptr_t)15;
         const uintptr_t last = (A + (uintptr_t)n * P - 1) & ~(uintptr_t)15;
         uint8_t *slot = ring + (j % D) * SLOTB;
+        // byte offsets from a0 (wave-uniform) in 32 bits: one clamp per load
+        const uint32_t lim = (uint32_t)(last - a0);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int pb = (i * 1024 < SLOTB - 1024) ? i * 1024 : SLOTB - 1024;
-            uintptr_t src = a0 + (uintptr_t)slot_phys(pb + 16 * lane);
-            src = src < last ? src : last;
+            const uint32_t off = (uint32_t)slot_phys(pb + 16 * lane);
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(a0) + (off < lim ? off : lim);
             __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(slot + pb), 16, 0, 0);
         }
     };
