@@ -112,15 +112,30 @@ __device__ inline void bf16_vec_to_f32(const typename VecT<VW>::T &v, float *f) 
     }
 }
 
+// LDS of the absorption, one instance per vector width (shared by both row counts)
 template <int VW>
-__device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
+struct AbsorbSmem {
+    float qs[kAbsorbHeads][kMaxDh];
+    // row-group partials; a row group's stride is one float past a multiple of
+    // the bank count, so a wave's 8 row groups x 8 column groups write distinct banks
+    float red[AbsorbCfg<VW>::DG][kAbsorbHeads * kAbsorbCols + 1];
+};
+template <int VW>
+__device__ inline AbsorbSmem<VW> &absorb_smem() {
+    __shared__ AbsorbSmem<VW> sm;
+    return sm;
+}
+
+// RR rows per thread: A::RMAX covers d_h = kMaxDh, A::RMAX / 2 covers d_h <= kMaxDh / 2
+template <int VW, int RR>
+__device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
                                    int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
                                    float odd_scale, int bits) {
     using A = AbsorbCfg<VW>;
     using VT = typename VecT<VW>::T;
-    __shared__ float qs[kAbsorbHeads][kMaxDh];
-    __shared__ float red[A::DG][kAbsorbHeads][kAbsorbCols];
+    auto &qs = absorb_smem<VW>().qs;
+    auto &red = absorb_smem<VW>().red;
     const int tid = threadIdx.x, cg = tid % A::CG, dg = tid / A::CG;
     const int k0 = cblk * kAbsorbCols + cg * VW;
     const bool kin = k0 < G;                  // G % VW == 0: the group is all in or all out
@@ -141,9 +156,9 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
     load_q(0);
     // W_k rows of this thread: loads issued unconditionally from clamped addresses
     const uint16_t *wk = W_kv + (size_t)g * d_h * G + (kin ? k0 : 0);
-    VT wr[A::RMAX];
+    VT wr[RR];
 #pragma unroll
-    for (int i = 0; i < A::RMAX; ++i) {
+    for (int i = 0; i < RR; ++i) {
         const int d = dg + A::DG * i;
         wr[i] = *reinterpret_cast<const VT *>(wk + (size_t)(d < d_h ? d : d_h - 1) * G);
     }
@@ -152,9 +167,9 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
         for (int c = 0; c < VW; ++c)
             if (k0 + c < GP)
                 for (int h = n_q; h < nqp; ++h) qt[((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
-    float w[A::RMAX][VW];
+    float w[RR][VW];
 #pragma unroll
-    for (int i = 0; i < A::RMAX; ++i) {
+    for (int i = 0; i < RR; ++i) {
         bf16_vec_to_f32<VW>(wr[i], w[i]);
         const bool ok = kin && dg + A::DG * i < d_h;
 #pragma unroll
@@ -169,27 +184,34 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
             qs[j][d] = (j < nh && d < d_h) ? bf16_to_f32(qr[u]) : 0.0f;
         }
         __syncthreads();
-        for (int j = 0; j < nh; ++j) {
-            float a[VW];
+        // every head of the pass at once, straight-line (staged rows of heads
+        // past nh are zero; their partials are written and never read)
+        float a[kAbsorbHeads][VW];
 #pragma unroll
-            for (int c = 0; c < VW; ++c) a[c] = 0.0f;
+        for (int j = 0; j < kAbsorbHeads; ++j)
 #pragma unroll
-            for (int i = 0; i < A::RMAX; ++i) {
-                const int d = dg + A::DG * i;
+            for (int c = 0; c < VW; ++c) a[j][c] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < RR; ++i) {
+            const int d = dg + A::DG * i;
+#pragma unroll
+            for (int j = 0; j < kAbsorbHeads; ++j) {
                 const float qv = qs[j][d < kMaxDh ? d : kMaxDh - 1];
 #pragma unroll
-                for (int c = 0; c < VW; ++c) a[c] += w[i][c] * qv;
+                for (int c = 0; c < VW; ++c) a[j][c] += w[i][c] * qv;
             }
-#pragma unroll
-            for (int c = 0; c < VW; ++c) red[dg][j][cg * VW + c] = a[c];
         }
+#pragma unroll
+        for (int j = 0; j < kAbsorbHeads; ++j)
+#pragma unroll
+            for (int c = 0; c < VW; ++c) red[dg][j * kAbsorbCols + cg * VW + c] = a[j][c];
         __syncthreads();
         for (int o = tid; o < nh * kAbsorbCols; o += blockDim.x) {
             const int j = o / kAbsorbCols, col = o - j * kAbsorbCols;
             const int k = cblk * kAbsorbCols + col;
             if (k < GP) {
                 float sum = 0.0f;
-                for (int r = 0; r < A::DG; ++r) sum += red[r][j][col];
+                for (int r = 0; r < A::DG; ++r) sum += red[r][j * kAbsorbCols + col];
                 const int h = g * grp + hb + j;
                 const float sk = (k & 1) ? scale * odd_scale : scale;
                 qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP, bits)] = (_Float16)(k < G ? sum * sk : 0.0f);
@@ -197,6 +219,18 @@ __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cbl
         }
         __syncthreads();
     }
+}
+
+template <int VW>
+__device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
+                                   const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
+                                   int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
+                                   float odd_scale, int bits) {
+    using A = AbsorbCfg<VW>;
+    if (d_h <= A::DG * (A::RMAX / 2))   // uniform
+        absorb_rows<VW, A::RMAX / 2>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
+    else
+        absorb_rows<VW, A::RMAX>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
 }
 
 // Absorption launch of fsq_decode_attn: one CTA per (kv head, 64-column
