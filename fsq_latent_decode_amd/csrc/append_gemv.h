@@ -20,6 +20,25 @@ __device__ inline float dot8_bf16(u32x4 a, u32x4 b) {
     return s;
 }
 
+// Sum over the 64 lanes of a wave, in every lane, without LDS: quad swaps and
+// the half-row and row mirrors (DPP) leave each 16-lane row's sum in all of its
+// lanes; v_permlane16_swap and v_permlane32_swap then pair rows l, l ^ 1 and
+// halves l, l ^ 2 (each returns the two operands with rows exchanged).
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float wave_sum_dpp(float a) {
+    a += dpp_f32<0xB1>(a);    // quad_perm [1, 0, 3, 2]
+    a += dpp_f32<0x4E>(a);    // quad_perm [2, 3, 0, 1]
+    a += dpp_f32<0x141>(a);   // row_half_mirror
+    a += dpp_f32<0x140>(a);   // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Output byte j of tokens tb .. tb + NT - 1 (< n): the CPB = 8 / bits codes of
 // coordinates CPB j .. CPB j + CPB - 1 (past G: zero bits), code i of the byte
 // at bits i * bits (little-endian within the byte).
@@ -40,6 +59,12 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int c = 0; c < CPB; ++c) acc[t][c] = 0.0f;
+    // the destination row's length, requested ahead of the dot products' loads
+    // (a volatile read keeps it there rather than next to its use after the
+    // barrier, where its latency would add to the step)
+    const int64_t len_t = (lens != nullptr && (int)threadIdx.x < nt)
+                              ? *reinterpret_cast<const volatile int32_t *>(lens + tb + threadIdx.x)
+                              : 0;
     const int nv = C / 8;
     const u32x4 *ep[CPB];
     bool has[CPB];
@@ -80,8 +105,7 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int c = 0; c < CPB; ++c) {
-            float a = acc[t][c];
-            for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off);
+            const float a = wave_sum_dpp(acc[t][c]);
             if (lane == 0) red[wave][t][c] = a;
         }
     __syncthreads();
@@ -99,9 +123,8 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
         if (lens == nullptr) {
             row = (size_t)(tb + t);
         } else {
-            const int64_t len = lens[tb + t];
-            if (len < 1 || len > seq_cap) return;
-            row = (size_t)(tb + t) * (size_t)seq_cap + (size_t)(len - 1);
+            if (len_t < 1 || len_t > seq_cap) return;
+            row = (size_t)(tb + t) * (size_t)seq_cap + (size_t)(len_t - 1);
         }
         codes[row * P + j] = (uint8_t)byte;
     }

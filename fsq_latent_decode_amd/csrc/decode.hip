@@ -154,6 +154,14 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
         }
     };
     load_q(0);
+    // this thread's output in every pass: head j_t of the pass, column col_t;
+    // its operand position (integer divisions by runtime sizes) is computed
+    // here, while the loads are in flight, and pinned there
+    static_assert(kAbsorbHeads * kAbsorbCols == 256, "one output per thread and pass");
+    const int j_t = tid / kAbsorbCols, col_t = tid % kAbsorbCols, k_t = cblk * kAbsorbCols + col_t;
+    int pos_t = k_t < GP ? coord_to_pos(k_t, GP, bits) : 0;
+    asm volatile("" : "+v"(pos_t));
+    const float sk_t = (k_t & 1) ? scale * odd_scale : scale;
     // W_k rows of this thread: loads issued unconditionally from clamped addresses
     const uint16_t *wk = W_kv + (size_t)g * d_h * G + (kin ? k0 : 0);
     VT wr[RR];
@@ -206,16 +214,11 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
 #pragma unroll
             for (int c = 0; c < VW; ++c) red[dg][j * kAbsorbCols + cg * VW + c] = a[j][c];
         __syncthreads();
-        for (int o = tid; o < nh * kAbsorbCols; o += blockDim.x) {
-            const int j = o / kAbsorbCols, col = o - j * kAbsorbCols;
-            const int k = cblk * kAbsorbCols + col;
-            if (k < GP) {
-                float sum = 0.0f;
-                for (int r = 0; r < A::DG; ++r) sum += red[r][j * kAbsorbCols + col];
-                const int h = g * grp + hb + j;
-                const float sk = (k & 1) ? scale * odd_scale : scale;
-                qt[((size_t)b * nqp + h) * GP + coord_to_pos(k, GP, bits)] = (_Float16)(k < G ? sum * sk : 0.0f);
-            }
+        if (j_t < nh && k_t < GP) {
+            float sum = 0.0f;
+            for (int r = 0; r < A::DG; ++r) sum += red[r][j_t * kAbsorbCols + col_t];
+            const int h = g * grp + hb + j_t;
+            qt[((size_t)b * nqp + h) * GP + pos_t] = (_Float16)(k_t < G ? sum * sk_t : 0.0f);
         }
         __syncthreads();
     }
