@@ -755,7 +755,10 @@ __device__ inline half8 unpack_codes_centered(uint32_t w) {
 // gives the total, a prefix scan of the item counts locates item i.
 __device__ inline int stream_dyn_chunk(int64_t total, int ncta, int chunk_min) {
     constexpr int64_t q = 32 * kStreamWaves;
-    int64_t c = (total + ncta - 1) / ncta;
+    // ceil(total / ncta) by an fp64 division: total < 2^37 and ncta <= 2^10, so
+    // the correctly rounded quotient is within 2^-15 of the exact one, whose
+    // fraction is 0 or at least 2^-10: its floor is the integer quotient
+    int64_t c = (int64_t)floor((double)(total + ncta - 1) / (double)ncta);
     c = (c + q - 1) / q * q;
     return (int)(c < chunk_min ? chunk_min : c);
 }
@@ -838,7 +841,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     } else if (dyn_batch > 0) {
         int64_t t_lane;
         chunk = stream_dyn_lens(seq_lens, dyn_batch, seq_cap, ncta, chunk_arg, lane, t_lane);
-        const int n = (int)((t_lane + chunk - 1) / chunk);   // this lane's sequence's items
+        const int n = (int)(((uint32_t)t_lane + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // this lane's sequence's items (T < 2^31)
         int incl = n;
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(incl, off);
@@ -1380,6 +1383,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
 // shuffles. With few heads, blockIdx.z = c of NC CTAs per head each apply rows
 // [c d_h / NC, (c + 1) d_h / NC) of W_v (zbar is formed by each of them).
 constexpr int kMergeThreads = 1024;
+
+// Merge geometry of a launch, computed on the host so that the kernel's way to
+// its first loads has no integer division by runtime values. Quotients by
+// small divisors use q = (n ceil(2^k / d)) >> k, exact while n (d - 1) < 2^k.
+struct MergeGeom {
+    int DR;         // W_v rows per CTA (d_h / NC)
+    int tpr_log2;   // threads per W_v row: 1 << tpr_log2
+    int KG, SG;     // 8-coordinate groups of a partial row; split groups 1024 / KG
+    int kg_mul;     // ceil(2^16 / KG): tid / KG for tid < 1024 (KG <= 32)
+    int tpp_log2;   // level-two threads per position: 1 << tpp_log2
+    int ZS;         // zpart row stride (floats)
+    int g_mul;      // ceil(2^20 / (n_q / n_kv)): kv head of query head h < 64
+};
 constexpr int kMergeMaxS = 1024;
 
 template <int VW, int R>
@@ -1387,7 +1403,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
-    int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta) {
+    int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta, MergeGeom geo) {
     using VT = typename VecT<VW>::T;
     // W_v vectors per thread: a row is shared by TPR >= 4 threads (d_h <= 256),
     // so at most NVA per thread; NVT of them (at most 32 VGPRs) are held from the
@@ -1400,7 +1416,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
-    const int DR = d_h / (int)gridDim.z, d0 = (int)blockIdx.z * DR;   // this CTA's rows of W_v
+    const int DR = geo.DR, d0 = (int)blockIdx.z * DR;   // this CTA's rows of W_v
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
     const size_t srow = 1;   // rows between splits (head-major partials)
     // The sequence length is read first; the loads below are issued over all S
@@ -1412,13 +1428,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int32_t tl_raw = dyn_batch > 1 && (tid & 63) < dyn_batch ? seq_lens[tid & 63] : 0;
     // ---- issue: W_v row d, vectors part, part + TPR, ... (first: W_v is the
     // coldest data, read from HBM, while the partials were just written)
-    const int g = h / (n_q / n_kv);
+    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
     const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
-    int TPR = 4;
-    while (TPR * 2 * DR <= kMergeThreads && TPR < 64) TPR *= 2;
+    const int TPR = 1 << geo.tpr_log2;
     const int NV = G / VW;
-    const int d = d0 + tid / TPR, part = tid % TPR;
-    const bool drow = tid / TPR < DR;
+    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
+    const bool drow = (tid >> geo.tpr_log2) < DR;
     const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
     VT wv[NVT];
 #pragma unroll
@@ -1433,16 +1448,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
         const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
         const int64_t tl = tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
         chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
-        const int nsb = (int)((tb + chunk - 1) / chunk);
+        const int nsb = (int)(((uint32_t)tb + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // tb < 2^31
         s_rows = nsb < 1 ? 1 : nsb;
     }
     // ---- issue: partial rows sg + u SG and their (m, l)
-    const int KG = GP / 8, SG = kMergeThreads / KG;
+    const int KG = geo.KG, SG = geo.SG;
     // level 2 uses TPP threads per position; zpart rows are padded to ZS floats,
     // ZS = 64 / TPP (mod 32), so a wave's 64 reads fall on distinct bank pairs
-    const int TPP = GP <= 32 ? 32 : GP <= 64 ? 16 : GP <= 128 ? 8 : 4;
-    const int ZS = GP + (TPP == 32 ? 4 : 64 / TPP);
-    const int kg = tid % KG, sg = tid / KG;
+    const int TPP = 1 << geo.tpp_log2;
+    const int ZS = geo.ZS;
+    const int sg = (int)(((uint32_t)tid * (uint32_t)geo.kg_mul) >> 16), kg = tid - sg * KG;
     const bool zthr = sg < SG;
     const _Float16 *zp = part_z + ((size_t)b * n_q + h) * S * GP + kg * 8;
     const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + ((size_t)b * n_q + h) * S;
@@ -1454,9 +1469,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
         v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)ic * srow * GP);
         mr[u] = ml[(size_t)ic * srow];
     }
-    int64_t T = T_raw;
-    T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
-    const int ns = (int)((T + chunk - 1) / chunk);
+    // T < 2^31 and chunk < 2^30: the split count in 32-bit arithmetic
+    const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
+    const int ns = (int)((T + (uint32_t)chunk - 1u) / (uint32_t)chunk);
     if (ns == 0) {   // empty sequence (uniform): the output is zero
         for (int dd = tid; dd < DR; dd += kMergeThreads) o[d0 + dd] = 0;
         return;
@@ -1515,7 +1530,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     // r + TPP k, k < SG / TPP <= kL2 (all LDS reads issued before use)
     {
         constexpr int kL2 = 16;   // SG / TPP <= 13 for every GP
-        const int p = tid / TPP, r = tid % TPP;
+        const int p = tid >> geo.tpp_log2, r = tid & (TPP - 1);
         const int pc = p < GP ? p : 0;
         float gv[kL2], lv[kL2], zv[kL2];
 #pragma unroll
@@ -1594,11 +1609,22 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
     int nc = 1;
     while (nc < 4 && (int64_t)n_q * batch * nc * 2 <= 256 && d_h % (nc * 2) == 0 && d_h / (nc * 2) >= 16) nc *= 2;
     const dim3 mg(n_q, batch, nc);
+    MergeGeom geo;
+    geo.DR = d_h / nc;
+    geo.tpr_log2 = 2;   // TPR = 4, doubled while two rows' threads fit
+    while ((2 << geo.tpr_log2) * geo.DR <= kMergeThreads && (1 << geo.tpr_log2) < 64) ++geo.tpr_log2;
+    geo.KG = GP / 8;
+    geo.SG = SG;
+    geo.kg_mul = ((1 << 16) + geo.KG - 1) / geo.KG;
+    geo.tpp_log2 = GP <= 32 ? 5 : GP <= 64 ? 4 : GP <= 128 ? 3 : 2;
+    geo.ZS = GP + (geo.tpp_log2 == 5 ? 4 : 64 >> geo.tpp_log2);
+    const int grp = n_q / n_kv;
+    geo.g_mul = ((1 << 20) + grp - 1) / grp;
 #define FSQ_MERGE_CASE(VWX, RX)                                                                           \
     if (vw == VWX && r == RX) {                                                                           \
         decode_merge_kernel<VWX, RX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out, seq_cap, \
                                                                    G, GP, n_q, n_kv, d_h, chunk, S,       \
-                                                                   natural, bits, dyn_batch, ncta);       \
+                                                                   natural, bits, dyn_batch, ncta, geo);  \
         return hipGetLastError();                                                                         \
     }
 #define FSQ_MERGE_VW(VWX) FSQ_MERGE_CASE(VWX, 2) FSQ_MERGE_CASE(VWX, 4) FSQ_MERGE_CASE(VWX, 8)
