@@ -762,9 +762,44 @@ __device__ inline int stream_dyn_chunk(int64_t total, int ncta, int chunk_min) {
     c = (c + q - 1) / q * q;
     return (int)(c < chunk_min ? chunk_min : c);
 }
+// Cross-lane arithmetic without LDS (DPP and lane swaps; the compiler adds the
+// DPP hazard waits). update_dpp writes 0 where a lane is masked off or its
+// source lane lies outside the row.
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, BANKS, true);
+}
+// Sum over the 64 lanes, in every lane: quad swaps, half-row and row mirrors
+// leave each 16-lane row's sum in all its lanes; v_permlane16_swap and
+// v_permlane32_swap return the operand with rows (halves) exchanged.
+__device__ inline uint32_t wave_sum_u32(uint32_t a) {
+    a += dpp_u32<0xB1>(a);    // quad_perm [1, 0, 3, 2]
+    a += dpp_u32<0x4E>(a);    // quad_perm [2, 3, 0, 1]
+    a += dpp_u32<0x141>(a);   // row_half_mirror
+    a += dpp_u32<0x140>(a);   // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    a = r16[0] + r16[1];
+    const auto r32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    return r32[0] + r32[1];
+}
+// Sum of 64 lengths 0 <= v < 2^31 (exact: 16-bit halves summed in 32 bits)
 __device__ inline int64_t wave_sum64(int64_t v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    const uint32_t lo = wave_sum_u32((uint32_t)v & 0xFFFFu), hi = wave_sum_u32((uint32_t)((uint64_t)v >> 16));
+    return ((int64_t)hi << 16) + (int64_t)lo;
+}
+// Inclusive prefix sum over lanes 0..l: within rows by shifts 1, 2, 3 of the
+// input, then 4 and 8 of the partial sums (upper banks only), then each row's
+// last lane added to the rows after it (row_bcast:15 to rows 1, 3;
+// row_bcast:31 to rows 2, 3).
+__device__ inline uint32_t wave_scan_u32(uint32_t v) {
+    uint32_t x = v + dpp_u32<0x111>(v);
+    x += dpp_u32<0x112>(v);
+    x += dpp_u32<0x113>(v);
+    x += dpp_u32<0x114, 0xF, 0xE>(x);
+    x += dpp_u32<0x118, 0xF, 0xC>(x);
+    x += dpp_u32<0x142, 0xA, 0xF>(x);
+    x += dpp_u32<0x143, 0xC, 0xF>(x);
+    return x;
 }
 // lane's clamped length T_lane (0 past the batch) and the chunk
 __device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int batch, int64_t seq_cap,
@@ -842,18 +877,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         int64_t t_lane;
         chunk = stream_dyn_lens(seq_lens, dyn_batch, seq_cap, ncta, chunk_arg, lane, t_lane);
         const int n = (int)(((uint32_t)t_lane + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // this lane's sequence's items (T < 2^31)
-        int incl = n;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(incl, off);
-            if (lane >= off) incl += y;
-        }
+        const int incl = (int)wave_scan_u32((uint32_t)n);
         const int item = blockIdx.x;
         b = __builtin_popcountll(__ballot(incl <= item));   // sequences wholly before the item
         if (b >= dyn_batch) return;                         // no work left (uniform)
-        // wave-uniform values kept in scalar registers
+        // wave-uniform values kept in scalar registers (b is uniform: lane reads)
         chunk = __builtin_amdgcn_readfirstlane(chunk);
-        s = __builtin_amdgcn_readfirstlane(item - (__shfl(incl, b) - __shfl(n, b)));
-        T_dyn = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(t_lane, b));   // T < 2^31
+        s = item - (__builtin_amdgcn_readlane(incl, b) - __builtin_amdgcn_readlane(n, b));
+        T_dyn = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)t_lane, b);   // T < 2^31
+        if ((int64_t)s * chunk >= T_dyn) return;   // never taken (s < the sequence's items); keeps every tile inside it
         if (b != b_early) load_q(b);   // uniform
     } else {
         s = blockIdx.x;
