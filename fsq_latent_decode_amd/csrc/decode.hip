@@ -318,8 +318,10 @@ struct SplitCfg {
     static constexpr int RS = (GP / 2 + 63) / 64 * 64; // dwords per fp16 tile row
     static constexpr int kTileDw = kTile * RS;
     static constexpr int kZBytes = NW * kTileDw * 4;
-    static constexpr int kPBytes = NW * 2 * 64 * 16;
-    static_assert(32 * (GP + 8) * 2 <= kZBytes, "Q~ staging must fit in the tile region");
+    // the probability region also stages Q~ (32 rows of GP + 8 halves) before
+    // the first round: its first writes follow the max barrier, after every
+    // wave has read its Q~ operands, so the tiles need no barrier of their own
+    static constexpr int kPBytes = (NW * 2 * 64 * 16) > (32 * (GP + 8) * 2) ? (NW * 2 * 64 * 16) : (32 * (GP + 8) * 2);
 };
 
 // XOR swizzle (dword granularity) of the fp16 tile: the 16-byte row writes of
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     half8 qv[KB];
     {
         constexpr int QROW = GP + 8;
-        _Float16 *qsm = reinterpret_cast<_Float16 *>(zsm);   // the tile region is free here
+        _Float16 *qsm = reinterpret_cast<_Float16 *>(psm);   // free until the first max barrier
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
         constexpr int NQ16 = 32 * GP / 8;                    // 16-byte chunks
         constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
@@ -425,7 +427,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
             qv[kb] = *reinterpret_cast<const half8 *>(qsm + t * QROW + 16 * kb + 8 * hh);
-        __syncthreads();   // before the tile region is reused
     }
 
     float m_ref = -INFINITY, l_run = 0.0f;
