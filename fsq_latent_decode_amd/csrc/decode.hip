@@ -15,7 +15,9 @@
 //                       plus the append of each sequence's new token)
 //   decode_split_kernel one CTA per (token chunk, sequence, 32-head group):
 //                       codes -> registers (prefetched one round ahead) -> fp16
-//                       operands -> MFMA scores (all heads share z) -> LDS tile
+//                       operands -> MFMA scores (all heads share z); the codes
+//                       to an LDS tile (4-bit: the packed nibbles, read back
+//                       transposed by ds_read_b64_tr_b4; 2 and 8 bits: fp16)
 //                       -> online softmax (exp2) -> MFMA latent pooling ->
 //                       (m, l, zbar fp16); for long chunks decode_stream_kernel
 //                       (below) instead, split on the device for batches
@@ -76,6 +78,23 @@ __device__ inline half8 unpack_codes2(uint32_t w, int upper) {
     const u32x4 t = {v & m, (v >> 2) & m, (v >> 4) & m, (v >> 6) & m};
     return __builtin_bit_cast(half8, t);
 }
+
+// Codes of one packed dword as fp16 operands with five operations: nibbles at
+// bits 4..7 of each 16-bit half are masked in place rather than shifted down,
+// so the operand order is (c0,c4) (16 c1,16 c5) (c2,c6) (16 c3,16 c7) - the
+// order of unpack_codes with odd coordinates (or, for a transposed read, odd
+// source rows) 16 times larger; the other operand carries a factor 1/16 there.
+__device__ inline half8 unpack_codes_x16(uint32_t w) {
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, w8 = w >> 8;
+    const u32x4 t = {w & lo, w & hi, w8 & lo, w8 & hi};
+    return __builtin_bit_cast(half8, t);
+}
+
+// Row of token r (0..31) in the nibble tile: the 16 tokens a transposed read
+// gathers for one lane half are rows 16 hh .. 16 hh + 15.
+__device__ inline int tile_row(int r) { return ((r >> 3) << 2) | (r & 3) | (((r >> 2) & 1) << 4); }
+
+typedef int v2i32 __attribute__((vector_size(8)));
 
 // ---------------------------------------------------------------- absorb
 // q~[b, h, pos(k)] = scale * sum_d W_k[g d_h + d, k] q[b, h, d] for the heads h
@@ -318,6 +337,10 @@ struct SplitCfg {
     static constexpr int RS = (GP / 2 + 63) / 64 * 64; // dwords per fp16 tile row
     static constexpr int kTileDw = kTile * RS;
     static constexpr int kZBytes = NW * kTileDw * 4;
+    // 4-bit codes: per-wave nibble tiles (the packed rows, read back by
+    // ds_read_b64_tr_b4) instead of fp16 copies, a quarter of the LDS bytes
+    static constexpr int TSN = GP / 2 + 8;             // nibble-tile row stride: an odd number of 8-byte units
+    static constexpr int kNibBytes = NW * kTile * TSN;
     // the probability region also stages Q~ (32 rows of GP + 8 halves) before
     // the first round: its first writes follow the max barrier, after every
     // wave has read its Q~ operands, so the tiles need no barrier of their own
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     // the reference max may lag the true max by this much (log2 units) before the
     // accumulators are rescaled: p = 2^(s - m) stays <= 256, exact range for fp16
     constexpr float kRescaleSlack = 8.0f;
-    __shared__ __attribute__((aligned(16))) uint32_t zsm[C::kZBytes / 4];
+    __shared__ __attribute__((aligned(16))) uint32_t zsm[(BITS == 4 ? C::kNibBytes : C::kZBytes) / 4];
     __shared__ __attribute__((aligned(16))) uint8_t psm[C::kPBytes];
     __shared__ float tmax_s[NW][32], tsum_s[NW][32];
 
@@ -460,14 +483,23 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         // the padding G..GP-1 (bytes of the next row) meet zero q~ entries and
         // are never read back from the pooled sums; all codes are finite.
         // Scores are accumulated in units of 2^-24 (unpack_codes) and scaled
-        // when they enter the max and the exponent.
+        // when they enter the max and the exponent. 4-bit codes go to the
+        // wave's nibble tile as loaded (row tile_row(t), this lane's half) and
+        // are scored by unpack_codes_x16 against q~ with odd coordinates / 16.
+        if constexpr (BITS == 4) {
+            uint8_t *tdst = reinterpret_cast<uint8_t *>(zsm) + (wave * kTile + tile_row(t)) * C::TSN + hh * (GP / 4);
+#pragma unroll
+            for (int i = 0; i < KB / 2; ++i)
+                *reinterpret_cast<uint2 *>(tdst + 8 * i) = uint2{cur[2 * i], cur[2 * i + 1]};
+        }
         floatx16 sc = floatx16{};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const half8 z = BITS == 8   ? unpack_codes8(cur[2 * kb], cur[2 * kb + 1])
                             : BITS == 2 ? unpack_codes2(cur[kb >> 1], kb & 1)
-                                        : unpack_codes(cur[kb]);
-            *reinterpret_cast<half8 *>(zt_own + t * RS + ((8 * kb + 4 * hh) ^ zt_swz(t))) = z;
+                                        : unpack_codes_x16(cur[kb]);
+            if constexpr (BITS != 4)
+                *reinterpret_cast<half8 *>(zt_own + t * RS + ((8 * kb + 4 * hh) ^ zt_swz(t))) = z;
             sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc, 0, 0, 0);
         }
         float sv[16];
@@ -500,10 +532,14 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         }
         psum = halves_sum(psum);
         if (lane < 32) tsum_s[wave][t] = psum;
+        // pooling operands: with nibble tiles, in the order of unpack_codes_x16
+        // applied to a transposed read (pairs of rows, the second pair's
+        // weights / 16: they meet codes read 16x)
+        const _Float16 w16 = BITS == 4 ? (_Float16)0.0625f : (_Float16)1.0f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const half8 pv = {p[ks * 8 + 0], p[ks * 8 + 1], p[ks * 8 + 2], p[ks * 8 + 3],
-                              p[ks * 8 + 4], p[ks * 8 + 5], p[ks * 8 + 6], p[ks * 8 + 7]};
+            const half8 pv = {p[ks * 8 + 0], p[ks * 8 + 1], p[ks * 8 + 2] * w16, p[ks * 8 + 3] * w16,
+                              p[ks * 8 + 4], p[ks * 8 + 5], p[ks * 8 + 6] * w16, p[ks * 8 + 7] * w16};
             *reinterpret_cast<half8 *>(psm + ((wave * 2 + ks) * 64 + lane) * 16) = pv;
         }
         __syncthreads();
@@ -523,6 +559,46 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         // (phases 1 and 2 wrote them), so all NW tiles are pooled and the LDS
         // operand reads of tile w2 + 1 are issued before the MFMAs of tile w2.
         const int wv = __builtin_amdgcn_readfirstlane(wave);
+        if constexpr (BITS == 4) {
+            // transposed nibble reads: lane l addresses row 16 hh + (d & 8) +
+            // sigma^-1(d & 7) (d = l & 15; sigma as in tile_row) of a wave's
+            // tile, bytes 16 cb + 8 ((l >> 4) & 1): the A operand of block cb
+            // for the tile's 32 tokens in two k-steps, coordinates in natural
+            // order, matched by the probabilities' order above
+            const int dsrc = lane & 15;
+            const int rsrc = 16 * hh + (dsrc & 8) + (((dsrc & 3) << 1) | ((dsrc >> 2) & 1));
+            const uint8_t *trb = reinterpret_cast<const uint8_t *>(zsm) + rsrc * C::TSN + 8 * ((lane >> 4) & 1);
+            typedef __attribute__((address_space(3))) v2i32 lds_v2;
+            half8 pn[2][2];
+            v2i32 zn[2][CBW];
+            auto read_nib = [&](int w2, half8 (&pbo)[2], v2i32 (&zo)[CBW]) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    pbo[ks] = *reinterpret_cast<const half8 *>(psm + ((w2 * 2 + ks) * 64 + lane) * 16);
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) {
+                    const int cb = wv + NW * j;
+                    if (CB % NW == 0 || cb < CB)
+                        zo[j] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                            (lds_v2 *)(trb + w2 * kTile * C::TSN + 16 * cb));
+                }
+            };
+            read_nib(0, pn[0], zn[0]);
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const int cur_b = w2 & 1;
+                if (w2 + 1 < NW) read_nib(w2 + 1, pn[cur_b ^ 1], zn[cur_b ^ 1]);
+#pragma unroll
+                for (int j = 0; j < CBW; ++j) {
+                    if (CB % NW == 0 || wv + NW * j < CB) {
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zn[cur_b][j][0]),
+                                                                        pn[cur_b][0], acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zn[cur_b][j][1]),
+                                                                        pn[cur_b][1], acc[j], 0, 0, 0);
+                    }
+                }
+            }
+        } else {
         half8 pb[2][2];
         shortx4 za[2][2][CBW][2];
         auto read_ops = [&](int w2, half8 (&pbo)[2], shortx4 (&zao)[2][CBW][2]) {
@@ -561,11 +637,13 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
                     }
                 }
         }
+        }
         __syncthreads();   // the next round overwrites the tiles and probabilities
     }
 
-    // ---- epilogue: zbar = acc / l in operand-position order, fp16, stored from
-    // registers: each lane holds head t and, per block, 4 runs of 4 positions
+    // ---- epilogue: zbar = acc / l, fp16, stored from registers: each lane
+    // holds head t and, per block, 4 runs of 4 positions (natural coordinate
+    // order from nibble tiles; operand-position order from fp16 tiles)
     const float zscale = kCodeScale / l_run;   // codes n * 2^-24 pooled: zbar = 2^24 acc / l - L/2
     constexpr float kLevelOffset = (float)(1 << (BITS - 1));
     const int heads = (n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32;
@@ -597,16 +675,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 }
 
 // ----------------------------------------------------------- streaming split
-// Codes of one packed dword as fp16 operands with five operations: nibbles at
-// bits 4..7 of each 16-bit half are masked in place rather than shifted down,
-// so the operand order is (c0,c4) (16 c1,16 c5) (c2,c6) (16 c3,16 c7) - the
-// order of unpack_codes with odd coordinates (or, for a transposed read, odd
-// source rows) 16 times larger; the other operand carries a factor 1/16 there.
-__device__ inline half8 unpack_codes_x16(uint32_t w) {
-    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, w8 = w >> 8;
-    const u32x4 t = {w & lo, w & hi, w8 & lo, w8 & hi};
-    return __builtin_bit_cast(half8, t);
-}
 
 // The split kernel above makes its waves agree on one softmax state per round,
 // which costs three barriers and an fp16 copy of every tile in LDS per round;
@@ -633,8 +701,7 @@ __device__ inline half8 unpack_codes_x16(uint32_t w) {
 //      the tokens whose probabilities the lane already holds from step 2, so
 //      no probability crosses lanes.
 // LDS traffic per code byte: DMA write 1, row read 1, tile write 1, transposed
-// read 1 (the split kernel moves 8: an fp16 copy written and read back).
-// Pooled sums come out in natural coordinate order.
+// read 1. Pooled sums come out in natural coordinate order.
 template <int GP, int NW, int D, bool AL>
 struct StreamCfg {
     static constexpr int KB = GP / 16;                 // score k-blocks = dwords per lane half
@@ -664,11 +731,6 @@ struct StreamCfg {
 // The permutation is its own inverse.
 __device__ inline int slot_phys(int L) { return L ^ (((L >> 7) & 7) << 4); }
 
-// Row of token r (0..31) in the nibble tile: the 16 tokens a transposed read
-// gathers for one lane half are rows 16 hh .. 16 hh + 15.
-__device__ inline int tile_row(int r) { return ((r >> 3) << 2) | (r & 3) | (((r >> 2) & 1) << 4); }
-
-typedef int v2i32 __attribute__((vector_size(8)));
 
 // N transposed nibble reads (ds_read_b64_tr_b4) at LDS byte address a + 16 i,
 // issued back to back and waited for in the same asm block. Written in asm
@@ -1771,8 +1833,10 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
     _Float16 *pz = reinterpret_cast<_Float16 *>(ws + pl.off_acc);
     float *pml = reinterpret_cast<float *>(ws + pl.off_ml);
     const float scale = 1.4426950408889634f / sqrtf((float)d_h);
-    // the streaming kernel reads odd coordinates' codes 16x (unpack_codes_x16)
-    const float odd = pl.stream ? 0.0625f : 1.0f;
+    // 4-bit codes are read with odd coordinates 16x (unpack_codes_x16) by both
+    // split-K kernels, whose pooled sums then come out in natural coordinate order
+    const float odd = bits == 4 ? 0.0625f : 1.0f;
+    const int natural = bits == 4 ? 1 : 0;
     hipError_t e;
     // widest bf16 vector that divides G and the W_kv alignment
     const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
@@ -1828,7 +1892,7 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         if (e != hipSuccess) return e;
     }
     return launch_merge(pz, pml, W_kv, seq_lens, out, seq_cap, G, pl.GP, n_q, n_kv, d_h, batch, pl.chunk,
-                        pl.S > 0 ? pl.S : 1, pl.stream, bits, pl.dyn ? batch : 0, pl.ncta, st);
+                        pl.S > 0 ? pl.S : 1, natural, bits, pl.dyn ? batch : 0, pl.ncta, st);
 }
 
 // The key-reconstruction comparison: no absorption launch; the split kernel
