@@ -1802,13 +1802,17 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
                                const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
                                hipEvent_t ev1, int bits) {
+    // split kernel: 8-wave CTAs from GP 64 up, 4-wave CTAs below GP 128 (the plan's choice)
+    const bool nw8 = pl.waves == 8 && GP >= 64, nw4 = pl.waves == 4 && GP < 128;
     if (bits != 4) {   // 2- and 8-bit codes: the split kernel only
-        if (pl.stream || pl.waves != split_waves(GP)) return hipErrorInvalidValue;
-        constexpr int NW = GP >= 128 ? 8 : 4;
-        return bits == 2 ? launch_split_nw<GP, NW, 2>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
-                                                      batch, st, ev0, ev1)
-                         : launch_split_nw<GP, NW, 8>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
-                                                      batch, st, ev0, ev1);
+        if (pl.stream || !(nw8 || nw4)) return hipErrorInvalidValue;
+        if (bits == 2)
+            return nw8 ? launch_split_nw<GP, (GP >= 64 ? 8 : 4), 2>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1)
+                       : launch_split_nw<GP, (GP < 128 ? 4 : 8), 2>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                                     batch, st, ev0, ev1);
+        return nw8 ? launch_split_nw<GP, (GP >= 64 ? 8 : 4), 8>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1)
+                   : launch_split_nw<GP, (GP < 128 ? 4 : 8), 8>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                                 batch, st, ev0, ev1);
     }
     if (pl.stream) {
         if (pl.waves != kStreamWaves) return hipErrorInvalidValue;
@@ -1817,9 +1821,10 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
         return launch_stream_d<GP, D>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st,
                                       ev0, ev1);
     }
-    if (pl.waves != split_waves(GP)) return hipErrorInvalidValue;
-    return launch_split_nw<GP, (GP >= 128 ? 8 : 4), 4>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
-                                                       batch, st, ev0, ev1);
+    if (!(nw8 || nw4)) return hipErrorInvalidValue;
+    return nw8 ? launch_split_nw<GP, (GP >= 64 ? 8 : 4), 4>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st, ev0, ev1)
+               : launch_split_nw<GP, (GP < 128 ? 4 : 8), 4>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q,
+                                                             batch, st, ev0, ev1);
 }
 
 hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t *codes,

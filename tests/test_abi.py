@@ -223,6 +223,16 @@ def test_decode_plan_host_logic():
     assert not fsq.decode_plan(65, 16, 256, 65536)["device_split"]
     assert fsq.decode_plan(65, 16, 256, 65536)["kernel"] == "decode_stream_kernel"
     assert not fsq.decode_plan(1, 32, 256, 32768)["device_split"]
+    # widths 64 and 96: 8-wave split CTAs (256-token rounds, about 256 CTAs)
+    # once the work reaches 2 x 256 x 256 tokens, 4-wave CTAs (about 512) below
+    p = fsq.decode_plan(1, 32, 84, 131072)
+    assert p["kernel"] == "decode_split_kernel" and p["chunk"] == 512 and p["splits"] == 256
+    p = fsq.decode_plan(1, 32, 84, 65536)
+    assert p["chunk"] == 128 and p["splits"] == 512
+    p = fsq.decode_plan(1, 32, 32, 131072)
+    assert p["chunk"] == 256 and p["splits"] == 512
+    p = fsq.decode_plan(1, 32, 256, 32768)
+    assert p["chunk"] == 256 and p["splits"] == 128
     assert fsq.decode_plan(1, 32, 256, 0)["splits"] == 0
     with pytest.raises(fsq.FsqError):
         fsq.decode_plan(0, 32, 256, 10)

@@ -172,6 +172,11 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     (1, 4, 1, 128, 130, 90, [90]),               # G % 4 == 2: the same with 2-wide vectors
     (1, 32, 8, 128, 20, 131072, [131072]),       # G = 20 (409.6x, 10 B/token)
     (1, 32, 8, 128, 32, 131072, [131000]),       # G = 32 (256x, 16 B/token)
+    # widths 64 and 96 over >= 2 x 256 x 256 tokens of work: 8-wave split CTAs
+    # of two or more rounds (ragged, unaligned rows, a chunk ending mid-round)
+    (2, 32, 8, 128, 64, 65600, [65600, 40001]),
+    (1, 32, 8, 128, 84, 131072, [130999]),
+    (3, 16, 8, 128, 90, 50000, [50000, 9, 33333]),
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -357,6 +362,8 @@ def run_decode_levels(fsq, q_bits, packed, W_bits, lens, n_kv, levels):
     (1, 32, 8, 128, 128, 5000, [4999]),
     (2, 32, 8, 128, 20, 3000, [3000, 17]),
     (1, 32, 8, 128, 32, 70000, [70000]),
+    (2, 32, 8, 128, 64, 65600, [65600, 40001]),  # 8-wave split CTAs (widths 64, 96 on long work)
+    (1, 32, 8, 128, 84, 131072, [130999]),
 ])
 def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
     g = synth.rng(210, levels, G + cap)
