@@ -102,6 +102,30 @@ def _stream(stream) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
+def _stream_obj(stream):
+    """The call's stream as a torch stream object (the current stream for None;
+    a raw hipStream_t handle is wrapped, not copied)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+
+
+def _call_workspace(workspace, B, n_q, G, cap, device, stream) -> torch.Tensor:
+    """The caller's workspace, or a new one allocated on the call's stream.
+
+    A workspace made here is freed when the call returns, while its kernels may
+    still be queued. Allocating it under the call's stream hands the block back
+    to the caching allocator as that stream's memory, so it is reused only by
+    work ordered after those kernels on the same stream."""
+    if workspace is None:
+        with torch.cuda.stream(_stream_obj(stream)):
+            workspace = alloc_workspace(B, n_q, G, cap, device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    return workspace
+
+
 LEVEL_BITS = {4: 2, 16: 4, 256: 8}
 
 
@@ -191,9 +215,7 @@ def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes
     if x_new.shape[0] != B or tuple(E.shape) != (G, C):
         raise ValueError(f"x_new must be [{B}, C] and E [{G}, C], got {tuple(x_new.shape)}, "
                          f"{tuple(E.shape)}")
-    if workspace is None:
-        workspace = alloc_workspace(B, n_q, G, cap, q.device)
-    _dev(workspace, "workspace", torch.uint8, 1)
+    workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
     rc = lib().fsq_decode_step(x_new.data_ptr(), E.data_ptr(), q.data_ptr(), codes.data_ptr(),
                                W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q, n_kv,
                                d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
@@ -211,9 +233,7 @@ def fsq_decode_attn_levels(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Ten
     if levels not in LEVEL_BITS:
         raise ValueError(f"levels must be one of {sorted(LEVEL_BITS)}")
     B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels)
-    if workspace is None:
-        workspace = alloc_workspace(B, n_q, G, cap, q.device)
-    _dev(workspace, "workspace", torch.uint8, 1)
+    workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
     args = (q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, n_q,
             n_kv, d_h, G, levels, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
     if split_events is None:
@@ -234,9 +254,7 @@ def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, se
     (start, stop) (torch.cuda.Event with timing) the call goes through
     fsq_decode_attn_timed and the events bracket the split-K kernel."""
     B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
-    if workspace is None:
-        workspace = alloc_workspace(B, n_q, G, cap, q.device)
-    _dev(workspace, "workspace", torch.uint8, 1)
+    workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
     args = (q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
             B, n_q, n_kv, d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
     if split_events is None:
@@ -253,9 +271,7 @@ def fsq_decode_attn_recon(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tens
     """fsq_decode_attn computed with keys rebuilt per tile (K = Z W_k^T) instead of
     absorbed queries: the measured comparison. Same arguments and workspace."""
     B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
-    if workspace is None:
-        workspace = alloc_workspace(B, n_q, G, cap, q.device)
-    _dev(workspace, "workspace", torch.uint8, 1)
+    workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
     rc = lib().fsq_decode_attn_recon(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(),
                                      seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, cap,
                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
@@ -274,9 +290,7 @@ def fsq_decode_attn_rope(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tenso
     _dev(k_norm, "k_norm", torch.bfloat16, 1)
     if k_norm.shape[0] != d_h:
         raise ValueError(f"k_norm must be [{d_h}], got {tuple(k_norm.shape)}")
-    if workspace is None:
-        workspace = alloc_workspace(B, n_q, G, cap, q.device)
-    _dev(workspace, "workspace", torch.uint8, 1)
+    workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
     rc = lib().fsq_decode_attn_rope(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), k_norm.data_ptr(),
                                     seq_lens.data_ptr(), out.data_ptr(), B, n_q, n_kv, d_h, G, cap,
                                     float(rope_theta), float(norm_eps), workspace.data_ptr(),

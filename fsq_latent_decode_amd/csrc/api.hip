@@ -1,8 +1,10 @@
-// C ABI of the library (declared in include/fsq.h): validation, workspace
-// sizing and launches on the caller's stream. No device memory is allocated here.
+// C ABI of the library (declared in include/fsq.h): validation (validate.h,
+// host arithmetic only), workspace sizing and launches on the caller's stream.
+// No device memory is allocated here.
 #include "../../include/fsq.h"
 #include "common.h"
 #include "decode_plan.h"
+#include "validate.h"
 
 namespace fsq {
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
@@ -18,9 +20,6 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
                                void *workspace, hipStream_t st, const uint16_t *gamma, float eps,
                                float theta);
 }  // namespace fsq
-
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-static bool levels_ok(int levels) { return levels == 4 || levels == 16 || levels == 256; }
 
 extern "C" {
 
@@ -38,12 +37,8 @@ const char *fsq_status_string(int status) {
 
 int fsq_append_levels(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_tokens,
                       int32_t C, int32_t G, int32_t levels, void *stream) {
-    if (n_tokens < 0 || C < 1 || G < 1) return FSQ_ERR_SHAPE;
-    if (G > FSQ_MAX_G || C % 8 != 0 || !levels_ok(levels)) return FSQ_ERR_UNSUPPORTED;
-    if (n_tokens == 0) return FSQ_OK;
-    if (!x || !E || !codes) return FSQ_ERR_NULL;
-    if (!aligned16(x) || !aligned16(E)) return FSQ_ERR_UNSUPPORTED;
-    if (n_tokens > ((int64_t)1 << 31) * 32) return FSQ_ERR_UNSUPPORTED;
+    const int v = fsq::validate_append(x, E, codes, n_tokens, C, G, levels);
+    if (v != FSQ_OK || n_tokens == 0) return v;
     hipError_t e = fsq::launch_append(x, E, codes, n_tokens, C, G, levels, (hipStream_t)stream);
     return e == hipSuccess ? FSQ_OK : FSQ_ERR_HIP;
 }
@@ -55,7 +50,7 @@ int fsq_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n_t
 
 int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap, int32_t *kernel,
                          int32_t *splits, int64_t *chunk) {
-    if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return FSQ_ERR_SHAPE;
+    if (!fsq::decode_sizes_ok(batch, n_q, G, seq_cap)) return FSQ_ERR_SHAPE;
     if (!kernel || !splits || !chunk) return FSQ_ERR_NULL;
     const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
     *kernel = pl.stream ? (pl.dyn ? 2 : 1) : 0;
@@ -65,7 +60,7 @@ int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap,
 }
 
 size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap) {
-    if (batch < 1 || n_q < 1 || n_q > FSQ_MAX_NQ || G < 1 || G > FSQ_MAX_G || seq_cap < 0) return 0;
+    if (!fsq::decode_sizes_ok(batch, n_q, G, seq_cap)) return 0;
     return fsq::make_decode_plan(batch, n_q, G, seq_cap).total;
 }
 
@@ -75,19 +70,10 @@ static int decode_common(const uint16_t *q, const uint8_t *codes, const uint16_t
                          size_t workspace_bytes, void *stream, void *ev0, void *ev1,
                          const uint16_t *x_new = nullptr, const uint16_t *E = nullptr, int32_t C = 0,
                          int32_t levels = 16) {
-    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
-    if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
-    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH || !levels_ok(levels))
-        return FSQ_ERR_UNSUPPORTED;
-    if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
-    if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
-    if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
-    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap, levels == 16);
-    if (!workspace || workspace_bytes < fsq::make_decode_plan(batch, n_q, G, seq_cap).total ||
-        ((uintptr_t)workspace & 255u))
-        return FSQ_ERR_WORKSPACE;
-    // the merge kernel reduces at most 1024 splits (the plan gives <= 512 / batch + 1)
-    if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
+    fsq::DecodePlan pl;
+    const int v = fsq::validate_decode(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                                       workspace, workspace_bytes, levels, &pl);
+    if (v != FSQ_OK) return v;
     hipError_t e = fsq::launch_decode(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G,
                                       seq_cap, workspace, (hipStream_t)stream, (hipEvent_t)ev0,
                                       (hipEvent_t)ev1, x_new, E, C, levels);
@@ -136,12 +122,8 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
                     const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int32_t batch,
                     int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap,
                     void *workspace, size_t workspace_bytes, void *stream) {
-    if (C < 1) return FSQ_ERR_SHAPE;
-    if (batch >= 1 && n_q >= 1 && n_kv >= 1 && d_h >= 1 && G >= 1 && seq_cap >= 0) {
-        if (C % 8 != 0) return FSQ_ERR_UNSUPPORTED;
-        if (!x_new || !E) return FSQ_ERR_NULL;
-        if (!aligned16(x_new) || !aligned16(E)) return FSQ_ERR_UNSUPPORTED;
-    }
+    const int v = fsq::validate_step_append(x_new, E, batch, C, n_q, n_kv, d_h, G, seq_cap);
+    if (v != FSQ_OK) return v;
     return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
                          workspace_bytes, stream, nullptr, nullptr, x_new, E, C);
 }
@@ -151,17 +133,10 @@ static int recon_common(const uint16_t *q, const uint8_t *codes, const uint16_t 
                         int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,
                         size_t workspace_bytes, void *stream, const uint16_t *gamma, float eps,
                         float theta) {
-    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
-    if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
-    if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > 128 || d_h % 32 != 0 || n_q / n_kv > 32)
-        return FSQ_ERR_UNSUPPORTED;
-    if (!q || !W_kv || !seq_lens || !out || (!codes && seq_cap > 0)) return FSQ_ERR_NULL;
-    if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
-    if ((int64_t)batch * seq_cap > ((int64_t)1 << 40)) return FSQ_ERR_UNSUPPORTED;
-    const fsq::DecodePlan pl = fsq::make_decode_plan(batch, n_q, G, seq_cap);
-    if (!workspace || workspace_bytes < pl.total || ((uintptr_t)workspace & 255u))
-        return FSQ_ERR_WORKSPACE;
-    if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
+    fsq::DecodePlan pl;
+    const int v = fsq::validate_recon(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                                      workspace, workspace_bytes, &pl);
+    if (v != FSQ_OK) return v;
     hipError_t e = fsq::launch_decode_recon(pl, q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h,
                                             G, seq_cap, workspace, (hipStream_t)stream, gamma, eps,
                                             theta);
@@ -181,11 +156,8 @@ int fsq_decode_attn_rope(const uint16_t *q, const uint8_t *codes, const uint16_t
                          int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
                          int64_t seq_cap, float rope_theta, float norm_eps, void *workspace,
                          size_t workspace_bytes, void *stream) {
-    if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
-    if (!(rope_theta > 1.0f) || !(norm_eps >= 0.0f) || !(rope_theta < 1e30f) || !(norm_eps < 1.0f))
-        return FSQ_ERR_SHAPE;
-    if (d_h != 64 && d_h != 128) return FSQ_ERR_UNSUPPORTED;
-    if (!k_norm) return FSQ_ERR_NULL;
+    const int v = fsq::validate_rope_extra(k_norm, batch, n_q, n_kv, d_h, G, seq_cap, rope_theta, norm_eps);
+    if (v != FSQ_OK) return v;
     return recon_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
                         workspace_bytes, stream, k_norm, norm_eps, rope_theta);
 }

@@ -109,7 +109,7 @@ __device__ __attribute__((always_inline)) inline void append_gemv_body(int j, in
             if (lane == 0) red[wave][t][c] = a;
         }
     __syncthreads();
-    if (threadIdx.x < nt) {
+    if ((int)threadIdx.x < nt) {
         const int t = threadIdx.x;
         uint32_t byte = 0;
 #pragma unroll

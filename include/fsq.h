@@ -100,7 +100,9 @@ int fsq_append_levels(const uint16_t *x, const uint16_t *E, uint8_t *codes,
 /*
  * fsq_decode_workspace_bytes - device workspace that fsq_decode_attn needs for
  * these sizes (the absorbed queries and the split-K partial states).
- * Returns 0 for invalid sizes. Depends only on its arguments.
+ * Returns 0 for invalid sizes (batch < 1, n_q outside 1..FSQ_MAX_NQ, G outside
+ * 1..FSQ_MAX_G, seq_cap < 0, or batch * seq_cap > 2^40). Depends only on its
+ * arguments.
  */
 size_t fsq_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap);
 
@@ -129,7 +131,13 @@ int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap,
  * without key norm and RoPE). Keys and values are never written to memory.
  *   q        [batch, n_q, d_h]              bf16.
  *   codes    [batch, seq_cap, ceil(G/2)]    u8 packed cache (layout above),
- *                                           16-byte aligned.
+ *                                           16-byte aligned. The kernels read it
+ *                                           in aligned 16-byte units, so the
+ *                                           bytes from its end up to the next
+ *                                           16-byte boundary must be readable
+ *                                           memory (an allocation rounded up to
+ *                                           16 bytes, as PyTorch's are, is
+ *                                           enough); they never affect a result.
  *   W_kv     [2 * n_kv * d_h, G]            bf16; rows [0, n_kv d_h) are W_k and
  *                                           rows [n_kv d_h, 2 n_kv d_h) are W_v,
  *                                           each kv-head-major (d_h rows per head).
@@ -142,7 +150,8 @@ int fsq_decode_plan_info(int32_t batch, int32_t n_q, int32_t G, int64_t seq_cap,
  *                                           256-byte aligned; its content on entry
  *                                           is irrelevant and it is overwritten.
  * Sizes: batch >= 1, 1 <= n_q <= FSQ_MAX_NQ, n_kv >= 1, n_q % n_kv == 0,
- *        1 <= d_h <= FSQ_MAX_DH, 1 <= G <= FSQ_MAX_G, seq_cap >= 0.
+ *        1 <= d_h <= FSQ_MAX_DH, 1 <= G <= FSQ_MAX_G, seq_cap >= 0,
+ *        batch * seq_cap <= 2^40, batch <= 65535.
  * Arithmetic: fp16 MFMA operands (levels are exact in fp16; q~ rounded to
  * fp16 after scaling), fp32 accumulation and softmax, bf16 output.
  * Errors: FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED (d_h, G, n_q limits,
@@ -210,7 +219,9 @@ int fsq_decode_attn_levels_timed(const uint16_t *q, const uint8_t *codes, const 
  *   x_new    [batch, C]   bf16, 16-byte aligned: the new token of each sequence.
  *   E        [G, C]       bf16, 16-byte aligned.
  *   codes    [batch, seq_cap, ceil(G/2)] u8, 16-byte aligned; read, and row
- *                          seq_lens[b] - 1 of each sequence written.
+ *                          seq_lens[b] - 1 of each sequence written (the bytes
+ *                          up to the next 16-byte boundary after its end must be
+ *                          readable, as for fsq_decode_attn).
  *   q, W_kv, seq_lens, out, workspace: as fsq_decode_attn (workspace size from
  *                          fsq_decode_workspace_bytes(batch, n_q, G, seq_cap)).
  * Sizes: as fsq_decode_attn, and C >= 1 with C % 8 == 0.

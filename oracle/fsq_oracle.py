@@ -38,6 +38,11 @@ Readings of points the pages leave open:
     taken as already normalised and rotated at its own position.
 
 Every computation is fp64 on the exact values of the bf16 inputs.
+
+Parity unpinned: h_of_levels at L = 4 and 256 (the exact value of the bound h
+of Eq. 2 away from L = 16; only the interval that gives L levels is pinned).
+Every other function here is pinned by closed forms, invariants, library
+routines or brute force in tests/test_oracle_*.py.
 """
 from __future__ import annotations
 
@@ -65,7 +70,11 @@ def h_of_levels(levels: int) -> float:
     """Bound h of Eq. 2 for L levels. The pages print h only for L = 16 (7.5075,
     slides footnote); reading for L = 4 and 256 (the slides' backup frame "the
     grid size is an allocation choice"): h = 1.001 (L - 1) / 2, which gives
-    7.5075 at L = 16, with delta = 0.5 and levels -L/2 .. L/2 - 1."""
+    7.5075 at L = 16, with delta = 0.5 and levels -L/2 .. L/2 - 1.
+
+    PARITY UNPINNED at L = 4 and 256: no page value fixes h there. The tests pin
+    only that h lies in (L/2 - 1, L/2], the interval in which Eq. 2 yields
+    exactly L levels; any h inside it would pass them."""
     return 1.001 * (levels - 1) / 2.0
 
 

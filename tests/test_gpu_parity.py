@@ -2,11 +2,12 @@
 
 Bars (the workload's stated tolerances):
   * codes: bit-exact except that at most 1e-4 of them may differ, each by +-1,
-    and only where the oracle's bounded value u~ lies within TIE_TOL of a
-    half-integer (an fp32 rounding tie; TIE_TOL is derived in the design notes
-    from the fp32 accumulation error of E x);
-  * attention output: relative L2 error <= 5e-3 per call (fp32 accumulation,
-    fp16 operands, bf16 output).
+    and only where the oracle's bounded value u~ lies within tie_tol of a
+    half-integer, tie_tol being the worst-case error of the kernel's fp32
+    evaluation of u~ for that code (see tie_tol); at least one such flip is
+    allowed in any case (see check_codes);
+  * attention output: relative L2 error <= 5e-3 per sequence AND per (sequence,
+    query head) (fp32 accumulation, fp16 operands, bf16 output).
 """
 import math
 
@@ -21,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 5e-3
 FLIP_RATE = 1e-4
-TIE_TOL = 2e-3
+U32 = 2.0 ** -24          # unit roundoff of fp32
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +46,74 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
+def head_rel_l2(got, ref):
+    """Relative L2 error of every (sequence, head) output row: [B, n_q]."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    return num / den
+
+
+def check_decode(got, ref, lens, what=""):
+    """The attention bar, per sequence AND per (sequence, head).
+
+    A sequence of length 0 must give exactly zero. Otherwise both the relative
+    L2 error of the sequence's whole output [n_q, d_h] and that of every head's
+    row [d_h] must be below REL_L2: the per-head bound keeps an error confined
+    to one head (a wrong GQA mapping, a padded head group, one head's merge)
+    from hiding in the pooled norm. Returns and prints the worst of each."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    lens = np.asarray(lens)
+    worst_seq, worst_head, where = 0.0, 0.0, None
+    for b in range(len(lens)):
+        if lens[b] <= 0:
+            assert np.all(got[b] == 0), (what, b, "empty sequence must give 0")
+            continue
+        e = rel_l2(got[b], ref[b])
+        hr = head_rel_l2(got[b], ref[b])
+        h = int(np.argmax(hr))
+        worst_seq = max(worst_seq, e)
+        if hr[h] > worst_head:
+            worst_head, where = float(hr[h]), (b, h)
+        assert e < REL_L2, (what, b, e)
+        assert hr[h] < REL_L2, (what, "worst head", b, h, float(hr[h]))
+    print(f"{what}: worst sequence rel L2 {worst_seq:.2e}, worst (b, h) {where} {worst_head:.2e}")
+    return worst_seq, worst_head
+
+
+def tie_tol(x, E, levels=16):
+    """Per-code bound on |u~_fp32 - u~_exact| for the kernels' evaluation of Eq. 2.
+
+    u = E x: the bf16 products are exact in fp32, and along any path of the
+    kernels' sums (MFMA K-blocks of 16 accumulated in order, then at most two
+    cross-wave levels; or, for a few tokens, C/64 terms per lane and six
+    cross-lane levels) there are at most d = C/16 + 16 rounded fp32 additions,
+    so |du| <= gamma_d sum_i |x_i E_i| with gamma_d = d u / (1 - d u) (the
+    standard bound for a floating-point dot product, any summation order of
+    depth d). The bound then goes through u~ = h tanh(u + s) - delta, whose
+    slope is at most h, plus the fp32 rounding of u + s, tanhf (a few ulp),
+    the product by h and the subtraction: <= h (|u| + 8) u_32.
+    Returns an array of the codes' shape."""
+    h = orc.H_BOUND if levels == 16 else orc.h_of_levels(levels)
+    C = x.shape[1]
+    d = C / 16 + 16
+    gamma = d * U32 / (1 - d * U32)
+    s = np.abs(x) @ np.abs(E).T
+    u = x @ E.T
+    return h * gamma * s + h * (np.abs(u) + 8.0) * U32
+
+
 def check_codes(gpu_packed, x_bits, E_bits, G, levels=16):
-    """Compare GPU codes with the oracle's under the tie rule; return flip count."""
+    """Compare GPU codes with the oracle's under the tie rule; return (flips, the
+    largest tie distance among them).
+
+    A flip (a code differing by +-1) is allowed only where the oracle's u~ lies
+    within tie_tol of a half-integer, i.e. where the fp32 evaluation may land on
+    the other side of the rounding threshold. The number of flips must not
+    exceed 1e-4 of the codes, but one flip is allowed in any case: whether a
+    given case holds a code that close to a threshold is a matter of chance (a
+    few codes per million do at C = 4096), so for cases of fewer than 10^4
+    codes the allowance is one flip rather than the rate."""
     x = synth.bf16_bits_to_f64(x_bits)
     E = synth.bf16_bits_to_f64(E_bits)
     u = orc.projection(x, E)
@@ -62,11 +129,16 @@ def check_codes(gpu_packed, x_bits, E_bits, G, levels=16):
     n_bad = len(bad[0])
     assert np.all(np.abs(diff) <= 1), "a code differs by more than 1"
     assert n_bad <= max(1, int(FLIP_RATE * ref.size)), f"{n_bad} flipped codes"
+    max_dist = 0.0
     if n_bad:
         ut = orc.fsq_bound(u[bad], h=orc.H_BOUND if levels == 16 else orc.h_of_levels(levels))
         dist = np.abs(ut - (np.floor(ut) + 0.5))
-        assert np.all(dist < TIE_TOL), f"flip away from a tie: {dist.max()}"
-    return n_bad
+        tol = tie_tol(x, E, levels)[bad]
+        assert np.all(dist < tol), f"flip away from a tie: {dist.max()} (bound {tol.min()})"
+        max_dist = float(dist.max())
+        print(f"{n_bad} flips of {ref.size} codes at L={levels}, largest tie distance {max_dist:.2e} "
+              f"(bound there {float(tol[np.argmax(dist)]):.2e})")
+    return n_bad, max_dist
 
 
 def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0, levels=16):
@@ -126,8 +198,8 @@ def test_append_prefill_chunk_g84(fsq):
     E, _ = synth.layer_weights(w, 0)
     x = synth.layer_x(w, 0, w.append_tokens)
     got = run_append(fsq, x, E)
-    flips = check_codes(got, x, E, w.G)
-    print(f"g84 prefill chunk: {flips} of {x.shape[0] * w.G} codes at fp32 ties")
+    flips, dist = check_codes(got, x, E, w.G)
+    print(f"g84 prefill chunk: {flips} of {x.shape[0] * w.G} codes at fp32 ties (largest tie distance {dist:.2e})")
 
 
 # ------------------------------------------------------------------ decode
@@ -182,12 +254,7 @@ def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
     got = run_decode(fsq, q, packed, W, lens, n_kv)
     ref = oracle_decode(q, packed, W, lens, n_kv, G)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 # Caches whose capacity (batch x seq_cap) is large enough for the streaming
@@ -216,12 +283,7 @@ def test_decode_stream_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 13 + cap, B, n_q, n_kv, d_h, G, cap, lens)
     got = run_decode(fsq, q, packed, W, lens, n_kv)
     ref = oracle_decode(q, packed, W, lens, n_kv, G)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 # The device-side split of streaming calls (up to 64 sequences): the chunk
@@ -246,12 +308,7 @@ def test_decode_stream_device_split_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens)
     assert fsq.decode_plan(B, n_q, G, cap)["kernel"] == "decode_stream_kernel"
     got = run_decode(fsq, q, packed, W, lens, n_kv)
     ref = oracle_decode(q, packed, W, lens, n_kv, G)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 def test_decode_stream_deterministic(fsq):
@@ -291,12 +348,7 @@ def test_decode_recon_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 11 + cap, B, n_q, n_kv, d_h, G, cap, lens)
     got = run_decode_recon(fsq, q, packed, W, lens, n_kv)
     ref = oracle_decode(q, packed, W, lens, n_kv, G)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 def test_decode_recon_deterministic(fsq):
@@ -333,12 +385,7 @@ def test_decode_rope_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens, theta):
     got = run_decode_rope(fsq, q, packed, W, gam, lens, n_kv, theta, 1e-6)
     ref = orc.decode_attn_rope(synth.bf16_bits_to_f64(q), packed, synth.bf16_bits_to_f64(W), lens, n_kv,
                                G, synth.bf16_bits_to_f64(gam), 1e-6, theta)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 def run_decode_levels(fsq, q_bits, packed, W_bits, lens, n_kv, levels):
@@ -375,12 +422,7 @@ def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
     got = run_decode_levels(fsq, q, packed, W, lens, n_kv, levels)
     ref = orc.decode_attn(synth.bf16_bits_to_f64(q), packed, synth.bf16_bits_to_f64(W), lens, n_kv, G,
                           levels=levels)
-    for b in range(B):
-        if lens[b] == 0:
-            assert np.all(got[b] == 0)
-        else:
-            e = rel_l2(got[b], ref[b])
-            assert e < REL_L2, (b, e)
+    check_decode(got, ref, lens, f"B={B} n_q={n_q} G={G} cap={cap}")
 
 
 @pytest.mark.parametrize("levels", [4, 16, 256])
@@ -427,16 +469,55 @@ def test_levels_append_then_decode_at_the_g84_byte_budget(fsq, levels, G):
     ref_codes = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x), synth.bf16_bits_to_f64(E), levels), bits)
     ref = orc.decode_attn(synth.bf16_bits_to_f64(q), ref_codes[None], synth.bf16_bits_to_f64(W), [T], n_kv, G,
                           levels=levels)
-    assert rel_l2(got, ref) < REL_L2
+    check_decode(got, ref, [T], f"L={levels} G={G} append then decode")
 
 
-def test_decode_deterministic_and_split_invariant(fsq):
+def test_decode_deterministic(fsq):
+    """Run-to-run: the same call twice gives the same bits (fixed merge order)."""
     q, packed, W, lens = decode_case(5, 2, 32, 8, 128, 84, 9000, [9000, 4097])
     a = run_decode(fsq, q, packed, W, lens, 8)
     b = run_decode(fsq, q, packed, W, lens, 8)
     assert np.array_equal(a, b)
-    ref = oracle_decode(q, packed, W, lens, 8, 84)
-    assert rel_l2(a, ref) < REL_L2
+    check_decode(a, oracle_decode(q, packed, W, lens, 8, 84), lens, "deterministic")
+
+
+# Split-count invariance (the result must not depend on how the tokens are
+# split): one 9000-token sequence (a tail of 8 tokens in its last tile) placed
+# in caches of growing capacity. The plan depends on the capacity, so the same
+# tokens are split into different chunk lengths and counts, by 4- and 8-wave
+# CTAs of the split kernel and, at the largest capacity, by the streaming
+# kernel with the split chosen on the device. Rows past the length hold other
+# random codes and must not matter.
+@pytest.mark.parametrize("G,caps", [
+    (84, [9000, 70000, 200000, 400000]),
+    (256, [9000, 70000, 150000, 200000]),
+])
+def test_decode_split_count_invariance(fsq, G, caps):
+    T, n_q, n_kv, d_h = 9000, 32, 8, 128
+    g = synth.rng(220, G, 0)
+    q = synth.normal_bf16(g, (1, n_q, d_h))
+    W = synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G))
+    seq = synth.uniform_code_bytes(g, (1, T), G)
+    plans = [fsq.decode_plan(1, n_q, G, cap) for cap in caps]
+    keys = {(p["kernel"], p["device_split"], p["splits"], p["chunk"]) for p in plans}
+    assert len(keys) == len(caps), plans                       # four different splits
+    assert plans[-1]["kernel"] == "decode_stream_kernel" and plans[0]["kernel"] == "decode_split_kernel"
+    ref = oracle_decode(q, seq, W, [T], n_kv, G)
+    outs = []
+    for cap, plan in zip(caps, plans):
+        packed = np.concatenate([seq, synth.uniform_code_bytes(synth.rng(221, G, cap), (1, cap - T), G)], axis=1)
+        a = run_decode(fsq, q, packed, W, [T], n_kv)
+        assert np.array_equal(a, run_decode(fsq, q, packed, W, [T], n_kv)), plan   # and bitwise repeatable
+        check_decode(a, ref, [T], f"G={G} cap={cap} {plan}")
+        outs.append(a)
+    # the results of the different splits agree with each other within the bar,
+    # per head; they differ only by the rounding of the fp16 partial states
+    worst = 0.0
+    for i in range(len(outs)):
+        for j in range(i + 1, len(outs)):
+            worst = max(worst, float(head_rel_l2(outs[i][0], outs[j][0]).max()))
+    print(f"G={G}: largest per-head rel L2 between two splits {worst:.2e}")
+    assert worst < REL_L2
 
 
 def test_decode_workspace_reuse_across_calls(fsq):
@@ -446,7 +527,31 @@ def test_decode_workspace_reuse_across_calls(fsq):
     for seed in (11, 12):
         q, packed, W, lens = decode_case(seed, 1, 32, 8, 128, 256, 4096, [4096 - seed])
         got = run_decode(fsq, q, packed, W, lens, 8, workspace=ws)
-        assert rel_l2(got, oracle_decode(q, packed, W, lens, 8, 256)) < REL_L2
+        check_decode(got, oracle_decode(q, packed, W, lens, 8, 256), lens, f"workspace reuse, call {seed}")
+
+
+def test_decode_on_side_stream_without_workspace(fsq):
+    """A call on an explicit side stream with no workspace: the binding allocates
+    the workspace on that stream, so memory the current stream allocates and
+    writes right after the call returns cannot be the workspace the queued
+    kernels still use. Repeated with a raw stream handle."""
+    q, packed, W, lens = decode_case(13, 2, 32, 8, 128, 256, 20000, [20000, 777])
+    ref = oracle_decode(q, packed, W, lens, 8, 256)
+    nbytes = fsq.decode_workspace_bytes(2, 32, 256, 20000)
+    qd, cd, Wd = dev_bf16(q), dev_u8(packed), dev_bf16(W)
+    ld = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    torch.cuda.synchronize()
+    for as_handle in (False, True):
+        side = torch.cuda.Stream()
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        side.wait_stream(torch.cuda.current_stream())
+        fsq.fsq_decode_attn(qd, cd, Wd, ld, out, 8, stream=side.cuda_stream if as_handle else side)
+        junk = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xFF)                    # would overwrite a workspace taken from this stream's pool
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        check_decode(out.float().cpu().numpy().astype(np.float64), ref, lens, f"side stream (handle={as_handle})")
+        del junk
 
 
 def test_decode_workspace_too_small_raises(fsq):
@@ -471,7 +576,7 @@ def test_tiny_workload_append_then_decode(fsq):
     torch.cuda.synchronize()
     ref_codes = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x), synth.bf16_bits_to_f64(E)))
     ref = oracle_decode(q, ref_codes[None], W, [w.context], w.n_kv, w.G)
-    assert rel_l2(out.float().cpu().numpy(), ref) < REL_L2
+    check_decode(out.float().cpu().numpy(), ref, [w.context], "tiny workload")
 
 
 @pytest.mark.parametrize("name", ["qwen3_8b_g256", "qwen3_8b_g84"])
@@ -485,9 +590,7 @@ def test_decode_full_size_layer(fsq, name):
         packed = synth.layer_codes(w, layer)
         got = run_decode(fsq, q, packed, W, lens, w.n_kv)
         ref = oracle_decode(q, packed, W, lens, w.n_kv, w.G)
-        e = rel_l2(got, ref)
-        print(f"{name} layer {layer}: rel L2 {e:.2e}")
-        assert e < REL_L2
+        check_decode(got, ref, lens, f"{name} layer {layer}")
 
 
 def test_decode_ragged_batch_full_size(fsq):
@@ -499,8 +602,7 @@ def test_decode_ragged_batch_full_size(fsq):
     packed = synth.layer_codes(w, 0, lens=lens)
     got = run_decode(fsq, q, packed, W, lens, w.n_kv)
     ref = oracle_decode(q, packed, W, lens, w.n_kv, w.G)
-    for b in range(w.batch):
-        assert rel_l2(got[b], ref[b]) < REL_L2, b
+    check_decode(got, ref, lens, "ragged Qwen3-1.7B batch, layer 0")
 
 
 # ------------------------------------------------------------- decode step
@@ -550,11 +652,7 @@ def check_step(got_codes, got_out, x, E, q, packed, W, lens, n_kv, G):
     assert np.array_equal(got_codes[mask], packed[mask]), "a row other than the new token's changed"
     eff = np.minimum(np.maximum(lens, 0), cap)
     ref = oracle_decode(q, ref_cache, W, eff, n_kv, G)
-    for b in range(len(lens)):
-        if eff[b] == 0:
-            assert np.all(got_out[b] == 0)
-        else:
-            assert rel_l2(got_out[b], ref[b]) < REL_L2, b
+    check_decode(got_out, ref, eff, f"decode step B={len(lens)} G={G} cap={cap}")
 
 
 @pytest.mark.parametrize("B,C,n_q,n_kv,d_h,G,cap,lens", [
@@ -607,7 +705,7 @@ def test_million_token_workload_layer0(fsq):
     E_dev = dev_bf16(E)
     ref_cache = np.empty((w.context, w.P), np.uint8)
     gpu_cache = torch.zeros((w.context, w.P), dtype=torch.uint8, device="cuda")
-    flips = 0
+    flips, max_dist = 0, 0.0
     depth = 6
     with ThreadPoolExecutor(depth) as ex:
         futs = [ex.submit(synth.layer_x_chunk, w, 0, c, chunk) for c in range(min(depth, n_chunks))]
@@ -627,7 +725,9 @@ def test_million_token_workload_layer0(fsq):
                 assert np.all(np.abs(diff) <= 1), f"chunk {c}: a code differs by more than 1"
                 ut = orc.fsq_bound(u[bad])
                 dist = np.abs(ut - (np.floor(ut) + 0.5))
-                assert np.all(dist < TIE_TOL), f"chunk {c}: flip away from a tie ({dist.max()})"
+                tol = tie_tol(synth.bf16_bits_to_f64(x), Ef)[bad]
+                assert np.all(dist < tol), f"chunk {c}: flip away from a tie ({dist.max()})"
+                max_dist = max(max_dist, float(dist.max()))
             flips += len(bad[0])
     assert flips <= FLIP_RATE * w.context * w.G, f"{flips} flipped codes"
     # level statistics of FSQ(E x) (not uniform): every code value occurs
@@ -636,6 +736,6 @@ def test_million_token_workload_layer0(fsq):
     lens = synth.seq_lens(w)
     got = run_decode(fsq, q, ref_cache[None], W, lens, w.n_kv)
     want = oracle_decode(q, ref_cache[None], W, lens, w.n_kv, w.G)
-    e = rel_l2(got, want)
-    print(f"million-token layer 0: {flips} of {w.context * w.G} codes at fp32 ties, rel L2 {e:.2e}")
-    assert e < REL_L2
+    print(f"million-token layer 0: {flips} of {w.context * w.G} codes at fp32 ties "
+          f"(largest tie distance {max_dist:.2e})")
+    check_decode(got, want, lens, "million-token layer 0")

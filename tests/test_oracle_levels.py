@@ -26,6 +26,27 @@ def test_h_reading_reproduces_the_printed_value():
 
 
 @pytest.mark.parametrize("L", [4, 256])
+def test_h_reading_gives_exactly_L_levels(L):
+    """h at L = 4 and 256 is a reading and its exact value is parity unpinned:
+    the pages print h only for L = 16. What they do fix is that Eq. 2 rounds a
+    coordinate to L levels; with delta = 1/2 that holds exactly when h lies in
+    (L/2 - 1, L/2]. The reading lies there, and an h just outside gives a
+    different number of levels (so the pin fails a reading that does not
+    produce an L-level grid, but not one that moves h inside the interval)."""
+    h = orc.h_of_levels(L)
+    assert L / 2 - 1 < h <= L / 2
+    u = np.linspace(-15.0, 15.0, 300001)        # tanh < 1 strictly: the range of u~ stays open
+
+    def count(hh):
+        return len(np.unique(np.rint(orc.fsq_bound(u, h=hh))))
+
+    assert count(h) == L
+    assert count(L / 2) == L
+    assert count(L / 2 + 0.05) != L
+    assert count(L / 2 - 1 - 0.05) != L
+
+
+@pytest.mark.parametrize("L", [4, 256])
 def test_level_invariants(L):
     u = np.linspace(-12, 12, 200001)
     c = orc.fsq_codes(u, L)
