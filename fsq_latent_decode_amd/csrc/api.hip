@@ -6,6 +6,7 @@
 #include "decode_plan.h"
 #include "validate.h"
 
+
 namespace fsq {
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
                          int G, int levels, hipStream_t st);

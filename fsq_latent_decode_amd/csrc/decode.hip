@@ -146,11 +146,16 @@ __device__ inline AbsorbSmem<VW> &absorb_smem() {
 }
 
 // RR rows per thread: A::RMAX covers d_h = kMaxDh, A::RMAX / 2 covers d_h <= kMaxDh / 2
+// qlo > 0 (8-bit codes): q~ is also stored as a second fp16 term, the rounding
+// residual q~ - fp16(q~), at qt + qlo. With 256 levels the scores spread over
+// about a hundred log2 units and the softmax is nearly an argmax, where one
+// fp16 rounding of q~ (relative 2^-12) moves the leading weights by about 1%;
+// the two terms carry q~ to about 2^-22.
 template <int VW, int RR>
 __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
                                    int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
-                                   float odd_scale, int bits) {
+                                   float odd_scale, int bits, size_t qlo) {
     using A = AbsorbCfg<VW>;
     using VT = typename VecT<VW>::T;
     auto &qs = absorb_smem<VW>().qs;
@@ -193,7 +198,10 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
     if (g == 0 && dg == 0)
         for (int c = 0; c < VW; ++c)
             if (k0 + c < GP)
-                for (int h = n_q; h < nqp; ++h) qt[((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
+                for (int h = n_q; h < nqp; ++h) {
+                    qt[((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
+                    if (qlo) qt[qlo + ((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
+                }
     float w[RR][VW];
 #pragma unroll
     for (int i = 0; i < RR; ++i) {
@@ -237,7 +245,16 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
             float sum = 0.0f;
             for (int r = 0; r < A::DG; ++r) sum += red[r][j_t * kAbsorbCols + col_t];
             const int h = g * grp + hb + j_t;
-            qt[((size_t)b * nqp + h) * GP + pos_t] = (_Float16)(k_t < G ? sum * sk_t : 0.0f);
+            // the fp32 product is kept as such (not folded with the fp16
+            // conversion into one mixed-precision FMA, which rounds once), so
+            // that every instantiation - with or without the second term -
+            // rounds q~ the same way: the decode step and the two-call path
+            // must give identical bits
+            float v = k_t < G ? sum * sk_t : 0.0f;
+            asm volatile("" : "+v"(v));
+            const _Float16 hi = (_Float16)v;
+            qt[((size_t)b * nqp + h) * GP + pos_t] = hi;
+            if (qlo) qt[qlo + ((size_t)b * nqp + h) * GP + pos_t] = (_Float16)(v - (float)hi);
         }
         __syncthreads();
     }
@@ -247,12 +264,12 @@ template <int VW>
 __device__ __attribute__((always_inline)) inline void absorb_body(int g, int cblk, int b, const uint16_t *__restrict__ q,
                                    const uint16_t *__restrict__ W_kv, _Float16 *__restrict__ qt,
                                    int G, int GP, int n_q, int nqp, int n_kv, int d_h, float scale,
-                                   float odd_scale, int bits) {
+                                   float odd_scale, int bits, size_t qlo) {
     using A = AbsorbCfg<VW>;
     if (d_h <= A::DG * (A::RMAX / 2))   // uniform
-        absorb_rows<VW, A::RMAX / 2>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
+        absorb_rows<VW, A::RMAX / 2>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits, qlo);
     else
-        absorb_rows<VW, A::RMAX>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
+        absorb_rows<VW, A::RMAX>(g, cblk, b, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits, qlo);
 }
 
 // Absorption launch of fsq_decode_attn: one CTA per (kv head, 64-column
@@ -262,12 +279,12 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ W_kv,
                                                      _Float16 *__restrict__ qt, int G, int GP,
                                                      int n_q, int nqp, int n_kv, int d_h, float scale,
-                                                     float odd_scale, int bits) {
+                                                     float odd_scale, int bits, size_t qlo) {
     const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
     int r = blockIdx.x;
     const int g = r % n_kv;
     r /= n_kv;
-    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits);
+    absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, bits, qlo);
 }
 
 // ---------------------------------------------------------- decode step
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int
         int r = bx - n_app;
         const int g = r % n_kv;
         r /= n_kv;
-        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, 4);
+        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, 4, 0);
     }
 }
 
@@ -356,7 +373,7 @@ template <int GP, int NW, bool AL, int BITS>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
-    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S) {
+    float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk, int S, size_t qlo) {
     using C = SplitCfg<GP, NW>;
     constexpr int KB = C::KB, CB = C::CB, CBW = C::CBW, RS = C::RS;
     constexpr int HB = GP * BITS / 16;       // bytes of a lane's half of a token row
@@ -418,6 +435,14 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     // once per CTA into LDS (rows padded to GP + 8 halves for conflict-free
     // 16-byte reads), then each wave takes its B operands from there
     half8 qv[KB];
+    // 8-bit codes: the residual term of q~ (see absorb_rows), B operands read
+    // straight from global memory, issued with the first tile's loads
+    half8 qvl[BITS == 8 ? KB : 1];
+    if constexpr (BITS == 8) {
+        const _Float16 *ql = qt + qlo + ((size_t)b * nqp + hg * 32 + t) * GP + 8 * hh;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qvl[kb] = *reinterpret_cast<const half8 *>(ql + 16 * kb);
+    }
     {
         constexpr int QROW = GP + 8;
         _Float16 *qsm = reinterpret_cast<_Float16 *>(psm);   // free until the first max barrier
@@ -501,6 +526,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             if constexpr (BITS != 4)
                 *reinterpret_cast<half8 *>(zt_own + t * RS + ((8 * kb + 4 * hh) ^ zt_swz(t))) = z;
             sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qv[kb], sc, 0, 0, 0);
+            if constexpr (BITS == 8) sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, qvl[kb], sc, 0, 0, 0);
         }
         float sv[16];
         float tmax = -INFINITY;
@@ -1737,6 +1763,7 @@ static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, cons
                                   const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                   int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
+    const size_t qlo = BITS == 8 ? (size_t)batch * pl.nqp * pl.GP : 0;
     dim3 grid(pl.S, batch, pl.nqp / 32);
     dim3 block(NW * 64);
     // whole-dword vector loads when every token row starts on a 16-byte boundary
@@ -1746,10 +1773,10 @@ static hipError_t launch_split_nw(const DecodePlan &pl, const _Float16 *qt, cons
     auto k = al ? decode_split_kernel<GP, NW, kCanAl, BITS> : decode_split_kernel<GP, NW, false, BITS>;
     if (ev0 && ev1)   // timed launch: events bracket this kernel's execution
         hipExtLaunchKernelGGL(k, grid, block, 0, st, ev0, ev1, 0, qt, codes, seq_lens, pz, pml,
-                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S);
+                              seq_cap, G, n_q, pl.nqp, pl.chunk, pl.S, qlo);
     else
         k<<<grid, block, 0, st>>>(qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, pl.nqp, pl.chunk,
-                                  pl.S);
+                                  pl.S, qlo);
     return hipGetLastError();
 }
 
@@ -1842,6 +1869,9 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
     // split-K kernels, whose pooled sums then come out in natural coordinate order
     const float odd = bits == 4 ? 0.0625f : 1.0f;
     const int natural = bits == 4 ? 1 : 0;
+    // 8-bit codes: the second term of q~ follows the first (the workspace's
+    // q~ region holds two)
+    const size_t qlo = bits == 8 ? (size_t)batch * pl.nqp * pl.GP : 0;
     hipError_t e;
     // widest bf16 vector that divides G and the W_kv alignment
     const int vw = ((G & 7) == 0 && ((uintptr_t)W_kv & 15) == 0)  ? 8
@@ -1869,10 +1899,10 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
         const dim3 ag((unsigned)n_abs);
         switch (vw) {
-            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
-            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
-            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits); break;
-            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits);
+            case 8: absorb_kernel<8><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits, qlo); break;
+            case 4: absorb_kernel<4><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits, qlo); break;
+            case 2: absorb_kernel<2><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits, qlo); break;
+            default: absorb_kernel<1><<<ag, 256, 0, st>>>(q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, bits, qlo);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

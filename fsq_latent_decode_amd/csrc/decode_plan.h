@@ -88,7 +88,8 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     p.S = (int)((seq_cap + p.chunk - 1) / p.chunk);
     const int S1 = p.S > 0 ? p.S : 1;
     p.off_qt = 0;
-    p.off_acc = align256((size_t)batch * p.nqp * p.GP * 2);
+    // q~ in fp16, two terms (8-bit codes use the second: the rounding residual)
+    p.off_acc = align256((size_t)batch * p.nqp * p.GP * 2 * 2);
     p.off_ml = p.off_acc + align256((size_t)batch * S1 * n_q * p.GP * 2);   // fp16 zbar
     p.total = p.off_ml + align256((size_t)batch * S1 * n_q * 2 * 4);
     return p;

@@ -41,12 +41,11 @@ inline bool decode_sizes_ok(int32_t batch, int32_t n_q, int32_t G, int64_t seq_c
            cache_rows_ok(batch, seq_cap);
 }
 
-// fsq_decode_attn, _levels, _timed and (with x_new, E, C) fsq_decode_step: on
-// FSQ_OK *plan is the plan the launch uses.
-inline int validate_decode(const void *q, const void *codes, const void *W_kv, const void *seq_lens,
-                           const void *out, int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h,
-                           int32_t G, int64_t seq_cap, const void *workspace, size_t workspace_bytes,
-                           int32_t levels, DecodePlan *plan) {
+// Everything fsq_decode_attn checks except the workspace: on FSQ_OK *plan is
+// the plan the launch uses and *ws_need the workspace bytes it needs.
+inline int validate_decode_args(const void *q, const void *codes, const void *W_kv, const void *seq_lens,
+                                const void *out, int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h,
+                                int32_t G, int64_t seq_cap, int32_t levels, DecodePlan *plan, size_t *ws_need) {
     if (batch < 1 || n_q < 1 || n_kv < 1 || d_h < 1 || G < 1 || seq_cap < 0) return FSQ_ERR_SHAPE;
     if (n_q % n_kv != 0) return FSQ_ERR_SHAPE;
     if (n_q > FSQ_MAX_NQ || G > FSQ_MAX_G || d_h > FSQ_MAX_DH || !levels_ok(levels))
@@ -55,12 +54,25 @@ inline int validate_decode(const void *q, const void *codes, const void *W_kv, c
     if (seq_cap > 0 && !aligned16(codes)) return FSQ_ERR_UNSUPPORTED;
     if (!cache_rows_ok(batch, seq_cap)) return FSQ_ERR_UNSUPPORTED;
     const DecodePlan pl = make_decode_plan(batch, n_q, G, seq_cap, levels == 16);
-    if (!workspace || workspace_bytes < make_decode_plan(batch, n_q, G, seq_cap).total ||
-        ((uintptr_t)workspace & 255u))
-        return FSQ_ERR_WORKSPACE;
     // the merge kernel reduces at most 1024 splits (the plan gives <= 512 / batch + 1)
     if (pl.S > 1024 || batch > 65535) return FSQ_ERR_UNSUPPORTED;
     if (plan) *plan = pl;
+    // the workspace size does not depend on the code width (fsq_decode_workspace_bytes)
+    if (ws_need) *ws_need = make_decode_plan(batch, n_q, G, seq_cap).total;
+    return FSQ_OK;
+}
+
+// fsq_decode_attn, _levels, _timed and (with x_new, E, C) fsq_decode_step: on
+// FSQ_OK *plan is the plan the launch uses.
+inline int validate_decode(const void *q, const void *codes, const void *W_kv, const void *seq_lens,
+                           const void *out, int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h,
+                           int32_t G, int64_t seq_cap, const void *workspace, size_t workspace_bytes,
+                           int32_t levels, DecodePlan *plan) {
+    size_t need = 0;
+    const int v = validate_decode_args(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, levels,
+                                       plan, &need);
+    if (v != FSQ_OK) return v;
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return FSQ_ERR_WORKSPACE;
     return FSQ_OK;
 }
 

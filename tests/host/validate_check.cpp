@@ -43,7 +43,7 @@ static void check_plan(const DecodePlan &p, int32_t batch, int32_t n_q, int32_t 
     const size_t S1 = p.S > 0 ? (size_t)p.S : 1;
     EXPECT(p.off_qt == 0);
     EXPECT(p.off_acc % 256 == 0 && p.off_ml % 256 == 0 && p.total % 256 == 0);
-    EXPECT(p.off_acc >= (size_t)batch * p.nqp * p.GP * 2);
+    EXPECT(p.off_acc >= (size_t)batch * p.nqp * p.GP * 2 * 2);   // q~ in two fp16 terms
     EXPECT(p.off_ml - p.off_acc >= (size_t)batch * S1 * n_q * p.GP * 2);
     EXPECT(p.total - p.off_ml >= (size_t)batch * S1 * n_q * 2 * 4);
 }
