@@ -17,7 +17,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
            "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels",
-           "fsq_decode_attn_levels_timed", "fsq_decode_plan_info")
+           "fsq_decode_attn_levels_timed", "fsq_decode_plan_info", "fsq_decode_attn_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # FSQ_NOALLOC_SCRATCH_BYTES in include/fsq.h
 
 FSQ_OK, FSQ_ERR_NULL, FSQ_ERR_SHAPE, FSQ_ERR_UNSUPPORTED, FSQ_ERR_WORKSPACE, FSQ_ERR_HIP = range(6)
 
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_attn_levels.restype = ctypes.c_int
         L.fsq_decode_attn_levels_timed.argtypes = L.fsq_decode_attn_levels.argtypes + [vp, vp]
         L.fsq_decode_attn_levels_timed.restype = ctypes.c_int
+        L.fsq_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, vp]
+        L.fsq_decode_attn_noalloc.restype = ctypes.c_int
         f32 = ctypes.c_float
         L.fsq_decode_attn_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, f32,
                                            vp, sz, vp]
@@ -262,6 +266,20 @@ def fsq_decode_attn(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor, se
     else:
         ev = [_event_handle(e) for e in split_events]
         _check(lib().fsq_decode_attn_timed(*args, ev[0], ev[1]), "fsq_decode_attn_timed")
+    return out
+
+
+def fsq_decode_attn_noalloc(q: torch.Tensor, codes: torch.Tensor, W_kv: torch.Tensor,
+                            seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int, stream=None) -> torch.Tensor:
+    """fsq_decode_attn with the library's fixed per-GPU scratch area as the
+    workspace (no allocation by the library or here): for callers that cannot
+    allocate. Calls that may overlap on one GPU share that area and must be
+    serialised by the caller. Raises FsqError (FSQ_ERR_WORKSPACE) when the sizes
+    need more than NOALLOC_SCRATCH_BYTES of workspace."""
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
+    rc = lib().fsq_decode_attn_noalloc(q.data_ptr(), codes.data_ptr(), W_kv.data_ptr(), seq_lens.data_ptr(),
+                                       out.data_ptr(), B, n_q, n_kv, d_h, G, cap, _stream(stream))
+    _check(rc, "fsq_decode_attn_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include "decode_plan.h"
 #include "validate.h"
 
+#include <mutex>
 
 namespace fsq {
 hipError_t launch_append(const uint16_t *x, const uint16_t *E, uint8_t *codes, int64_t n, int C,
@@ -21,6 +22,36 @@ hipError_t launch_decode_recon(const DecodePlan &pl, const uint16_t *q, const ui
                                void *workspace, hipStream_t st, const uint16_t *gamma, float eps,
                                float theta);
 }  // namespace fsq
+
+// Scratch memory of fsq_decode_attn_noalloc: the decode workspace (absorbed
+// queries, split partials) of callers that cannot allocate. A file-scope
+// device array, one copy per GPU the library is loaded on, kept until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it names a stand-in, not device memory): the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that pointer is passed to kernels.
+static_assert(FSQ_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[FSQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use); nullptr
+// if the device cannot be queried or its copy not located.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
 
 extern "C" {
 
@@ -87,6 +118,23 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
                     size_t workspace_bytes, void *stream) {
     return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
                          workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int fsq_decode_attn_noalloc(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                            const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
+                            int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *stream) {
+    // sizes first (as fsq_decode_attn would check them), then the scratch
+    // capacity, and only then the device's scratch address: an invalid or
+    // oversized call touches no HIP state
+    size_t need = 0;
+    const int v = fsq::validate_decode_args(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap,
+                                            16, nullptr, &need);
+    if (v != FSQ_OK) return v;
+    if (need > (size_t)FSQ_NOALLOC_SCRATCH_BYTES) return FSQ_ERR_WORKSPACE;
+    void *ws = device_scratch();
+    if (!ws) return FSQ_ERR_HIP;
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, ws,
+                         FSQ_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 int fsq_decode_attn_levels(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,

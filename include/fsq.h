@@ -165,6 +165,34 @@ int fsq_decode_attn(const uint16_t *q, const uint8_t *codes, const uint16_t *W_k
                     void *stream);
 
 /*
+ * fsq_decode_attn_noalloc - fsq_decode_attn for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Same computation, kernels and results as fsq_decode_attn with the same
+ * arguments (bit for bit); the workspace is instead a fixed scratch area inside
+ * the library, FSQ_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from
+ * the library's loading until the process ends. No allocation, free or
+ * allocating library routine is called. The scratch address of the current
+ * device is looked up on the first call on that device.
+ * Every call on one GPU shares that GPU's scratch area and leaves its last
+ * contents there (nothing in it needs to start at zero): calls that may
+ * overlap on one GPU (several streams, several host threads) race on it and
+ * must be serialised by the caller.
+ * Sizes and layouts: as fsq_decode_attn; the sizes must also satisfy
+ * fsq_decode_workspace_bytes(batch, n_q, G, seq_cap) <= FSQ_NOALLOC_SCRATCH_BYTES
+ * (e.g. batch 16 at seq_cap 65536 with n_q 16, G 256: 17.3 MB).
+ * Errors: as fsq_decode_attn; FSQ_ERR_WORKSPACE when the sizes need more
+ *         scratch than FSQ_NOALLOC_SCRATCH_BYTES (nothing is enqueued);
+ *         FSQ_ERR_HIP when the device or its scratch address cannot be queried.
+ */
+#define FSQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fsq_decode_attn_noalloc(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
+                            const int32_t *seq_lens, uint16_t *out,
+                            int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G,
+                            int64_t seq_cap, void *stream);
+
+/*
  * fsq_decode_attn_levels - fsq_decode_attn over a cache of L = levels codes
  * per coordinate (4, 16 or 256; rows of ceil(G b / 8) bytes, the layout
  * above), z_t = code_t - L/2. Same workspace size as fsq_decode_attn for the

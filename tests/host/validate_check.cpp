@@ -103,6 +103,15 @@ static void decode_cases() {
     EXPECT(decode(65536, 8, 8, 64, 32, 1, big) == FSQ_ERR_UNSUPPORTED);          // batch limit
     EXPECT(decode(2, 32, 8, 128, 84, ((int64_t)1 << 40) / 2 + 1, big) == FSQ_ERR_UNSUPPORTED);
     EXPECT(decode(INT32_MAX, FSQ_MAX_NQ, 1, FSQ_MAX_DH, FSQ_MAX_G, INT64_MAX, SIZE_MAX) == FSQ_ERR_UNSUPPORTED);
+    // the allocation-free entry point's capacity check: the per-layer
+    // workloads fit its scratch area, the layer-batched calls do not
+    size_t ws_need = 0;
+    EXPECT(fsq::validate_decode_args(P, P, P, P, P, 16, 16, 8, 128, 256, 65536, 16, nullptr, &ws_need) == FSQ_OK);
+    EXPECT(ws_need <= FSQ_NOALLOC_SCRATCH_BYTES);
+    EXPECT(fsq::validate_decode_args(P, P, P, P, P, 1, 32, 8, 128, 84, 1 << 20, 16, nullptr, &ws_need) == FSQ_OK);
+    EXPECT(ws_need <= FSQ_NOALLOC_SCRATCH_BYTES);
+    EXPECT(fsq::validate_decode_args(P, P, P, P, P, 36, 32, 8, 128, 84, 131072, 16, nullptr, &ws_need) == FSQ_OK);
+    EXPECT(ws_need > FSQ_NOALLOC_SCRATCH_BYTES);
     // the step's extra arguments
     EXPECT(fsq::validate_step_append(P, P, 1, 4096, 32, 8, 128, 84, 10) == FSQ_OK);
     EXPECT(fsq::validate_step_append(P, P, 1, 0, 32, 8, 128, 84, 10) == FSQ_ERR_SHAPE);
