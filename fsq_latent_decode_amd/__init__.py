@@ -13,7 +13,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
+# FSQ_LIBRARY_PATH: another build of the same library (A/B measurements);
+# the in-tree build by default
+_LIB_PATH = os.environ.get("FSQ_LIBRARY_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libfsq.so")
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
            "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels",

@@ -24,9 +24,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out` (the in-tree path by default); `defines`
+    are extra -D macros of compile-time variants (A/B measurements)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wextra", "-Werror",
            # keep hipcc from emitting packed-fp32 VALU forms
@@ -36,7 +38,7 @@ def build(verbose: bool = False) -> str:
            # the compiler copies every accumulator across each loop iteration
            "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"),
-           "-o", tmp] + [os.path.join(PKG, s) for s in SOURCES]
+           "-o", tmp] + [f"-D{d}" for d in defines] + [os.path.join(PKG, s) for s in SOURCES]
     res = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)
     msgs = [l for l in (res.stdout + res.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in l]
@@ -44,8 +46,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
