@@ -36,6 +36,16 @@ namespace fsq {
 
 constexpr int kTile = 32;        // tokens per wave and round (the score MFMA's M)
 
+// Lazy online softmax: the reference max m of a head is raised (and the
+// accumulators rescaled) only when a tile's max exceeds it by more than this
+// many log2 units, so the weights p = 2^(s - m) stay below 2^kRescaleSlack,
+// inside fp16's range (65504).
+#ifndef FSQ_RESCALE_SLACK
+#define FSQ_RESCALE_SLACK 15
+#endif
+constexpr float kRescaleSlack = (float)FSQ_RESCALE_SLACK;
+static_assert(FSQ_RESCALE_SLACK >= 1 && FSQ_RESCALE_SLACK <= 15, "p must stay below fp16's largest value");
+
 // Lane l's value combined with lane l ^ 32's through v_permlane32_swap (a VALU
 // exchange of the wave's halves; a shuffle would go through the LDS crossbar).
 // The swap returns the pair in an order that is the same for both lanes, so
@@ -380,9 +390,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     constexpr int ND = HB / 4;               // packed dwords per half (KB operands of 8 codes)
     constexpr int NLD = AL ? ND : ND + 1;   // dwords loaded per lane per tile
     static_assert(!AL || ND % 2 == 0, "8-byte loads of whole halves");
-    // the reference max may lag the true max by this much (log2 units) before the
-    // accumulators are rescaled: p = 2^(s - m) stays <= 256, exact range for fp16
-    constexpr float kRescaleSlack = 8.0f;
     __shared__ __attribute__((aligned(16))) uint32_t zsm[(BITS == 4 ? C::kNibBytes : C::kZBytes) / 4];
     __shared__ __attribute__((aligned(16))) uint8_t psm[C::kPBytes];
     __shared__ float tmax_s[NW][32], tsum_s[NW][32];
@@ -757,6 +764,103 @@ struct StreamCfg {
 // The permutation is its own inverse.
 __device__ inline int slot_phys(int L) { return L ^ (((L >> 7) & 7) << 4); }
 
+// Reads of a ring slot, written in asm. The slot is filled by direct-to-LDS
+// loads, and before any ordinary LDS read of that LDS object the compiler
+// waits for every such load in flight (vmcnt(0)), since it cannot tell which
+// slot a load targets: that would drain the ring on every tile. The kernel's
+// own s_waitcnt vmcnt already guarantees the slot being read is complete.
+// Each block waits for its own reads (lgkmcnt) before returning them.
+// a: LDS byte addresses.
+template <int N>
+__device__ __attribute__((always_inline)) inline void slot_read_b32(const uint32_t (&a)[N], uint32_t (&v)[N]) {
+    static_assert(N >= 1, "");
+    if constexpr (N >= 4) {
+        asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+        if constexpr (N > 4) {
+            uint32_t ar[N - 4], vr[N - 4];
+#pragma unroll
+            for (int i = 0; i < N - 4; ++i) ar[i] = a[4 + i];
+            slot_read_b32<N - 4>(ar, vr);
+#pragma unroll
+            for (int i = 0; i < N - 4; ++i) v[4 + i] = vr[i];
+        }
+    } else if constexpr (N == 3) {
+        asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2])
+                     : "memory");
+    } else if constexpr (N == 2) {
+        asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    } else {
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a[0]) : "memory");
+    }
+}
+template <int N>
+__device__ __attribute__((always_inline)) inline void slot_read_b128(const uint32_t (&a)[N], u32x4 (&v)[N]) {
+    static_assert(N >= 1 && N <= 4, "1..4 reads");
+    if constexpr (N == 4) {
+        asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    } else if constexpr (N == 3) {
+        asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2])
+                     : "memory");
+    } else if constexpr (N == 2) {
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(v[0]), "=&v"(v[1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    } else {
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a[0]) : "memory");
+    }
+}
+__device__ inline uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// This lane's half of token t's row (GP / 4 bytes, KB dwords) out of a ring
+// slot: 16-byte reads when rows are 16-byte aligned (AL), else the KB + 1
+// dwords around the half, funnel-shifted by the row's misalignment.
+template <int GP, bool AL>
+__device__ __attribute__((always_inline)) inline void slot_row(const uint8_t *slot, int t, int hh, int P, int mis,
+                                                               uint32_t (&cur)[GP / 16]) {
+    constexpr int KB = GP / 16;
+    if constexpr (AL) {
+        uint32_t a[KB / 4];
+        u32x4 v[KB / 4];
+#pragma unroll
+        for (int i = 0; i < KB / 4; ++i) a[i] = lds_addr(slot + slot_phys(t * P + hh * (GP / 4) + 16 * i));
+        slot_read_b128<KB / 4>(a, v);
+#pragma unroll
+        for (int i = 0; i < KB / 4; ++i) {
+            cur[4 * i + 0] = v[i].x;
+            cur[4 * i + 1] = v[i].y;
+            cur[4 * i + 2] = v[i].z;
+            cur[4 * i + 3] = v[i].w;
+        }
+    } else {
+        const int ab = mis + t * P + hh * (GP / 4);
+        const int a0 = ab & ~3, sh = (ab & 3) * 8;
+        uint32_t a[KB + 1], ld[KB + 1];
+#pragma unroll
+        for (int i = 0; i < KB + 1; ++i) a[i] = lds_addr(slot + slot_phys(a0 + 4 * i));
+        slot_read_b32<KB + 1>(a, ld);
+#pragma unroll
+        for (int i = 0; i < KB; ++i) cur[i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
+    }
+}
+
 
 // N transposed nibble reads (ds_read_b64_tr_b4) at LDS byte address a + 16 i,
 // issued back to back and waited for in the same asm block. Written in asm
@@ -914,7 +1018,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // subnormals), in plain log2 units from rebuilt keys (rescaled below)
     constexpr float kSS = RC ? 1.0f : kCodeScale;
     constexpr int WROW = GP + 8;   // rebuilt-key operand rows (halves), RC only
-    constexpr float kRescaleSlack = 8.0f;   // as in the split kernel: p <= 256
     // s_waitcnt immediates (gfx9 layout), only vmcnt waited on
     constexpr int kWaitAhead = (((D - 1) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 1) * NI) >> 4) << 14);
     constexpr int kWaitAll = (0x7 << 4) | (0xF << 8);
@@ -1137,25 +1240,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
                 const int64_t rem = cend - t0;
                 ntok[u] = rem < kTile ? (int)rem : kTile;
                 const uint8_t *slot = ring + ((j + u) % D) * SLOTB;
-                if (AL) {
-#pragma unroll
-                    for (int i = 0; i < KB / 4; ++i) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + slot_phys(t * P + hh * (GP / 4) + 16 * i));
-                        cur[u][4 * i + 0] = v.x;
-                        cur[u][4 * i + 1] = v.y;
-                        cur[u][4 * i + 2] = v.z;
-                        cur[u][4 * i + 3] = v.w;
-                    }
-                } else {
-                    const int mis = (int)((uintptr_t)(seq + (size_t)t0 * P) & 15);
-                    const int a = mis + t * P + hh * (GP / 4);
-                    const int a0 = a & ~3, sh = (a & 3) * 8;
-                    uint32_t ld[KB + 1];
-#pragma unroll
-                    for (int i = 0; i < KB + 1; ++i) ld[i] = *reinterpret_cast<const uint32_t *>(slot + slot_phys(a0 + 4 * i));
-#pragma unroll
-                    for (int i = 0; i < KB; ++i) cur[u][i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
-                }
+                slot_row<GP, AL>(slot, t, hh, P, AL ? 0 : (int)((uintptr_t)(seq + (size_t)t0 * P) & 15), cur[u]);
 #pragma unroll
                 for (int i = 0; i < KB / 2; ++i)
                     *reinterpret_cast<uint2 *>(tdst + u * 32 * TS + 8 * i) = uint2{cur[u][2 * i], cur[u][2 * i + 1]};
@@ -1261,25 +1346,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         // finite codes (stale slot bytes or the next row's): the former get
         // probability 0, the latter meet zero q~ entries and are never read back.
         uint32_t cur[KB];
-        if (AL) {
-#pragma unroll
-            for (int i = 0; i < KB / 4; ++i) {
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(slot + slot_phys(t * P + hh * (GP / 4) + 16 * i));
-                cur[4 * i + 0] = v.x;
-                cur[4 * i + 1] = v.y;
-                cur[4 * i + 2] = v.z;
-                cur[4 * i + 3] = v.w;
-            }
-        } else {
-            const int mis = (int)((uintptr_t)(seq + (size_t)t0 * P) & 15);
-            const int a = mis + t * P + hh * (GP / 4);
-            const int a0 = a & ~3, sh = (a & 3) * 8;
-            uint32_t ld[KB + 1];
-#pragma unroll
-            for (int i = 0; i < KB + 1; ++i) ld[i] = *reinterpret_cast<const uint32_t *>(slot + slot_phys(a0 + 4 * i));
-#pragma unroll
-            for (int i = 0; i < KB; ++i) cur[i] = (uint32_t)((((uint64_t)ld[i + 1] << 32) | ld[i]) >> sh);
-        }
+        slot_row<GP, AL>(slot, t, hh, P, AL ? 0 : (int)((uintptr_t)(seq + (size_t)t0 * P) & 15), cur);
 #pragma unroll
         for (int i = 0; i < KB / 2; ++i)
             *reinterpret_cast<uint2 *>(tdst + 8 * i) = uint2{cur[2 * i], cur[2 * i + 1]};
