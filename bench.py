@@ -38,6 +38,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 2 ** 20
 COMPARED = ("qwen3_8b_g256", "qwen3_8b_g84")   # workloads of the SDPA and key-reconstruction comparisons
+# workloads whose line carries the oracle's CPU baseline and in-run parity
+CPU_BASELINE_WORKLOADS = ("qwen3_8b_g256", "qwen3_8b_g84", "qwen3_1p7b_ragged", "qwen3_8b_g84_1m")
 
 
 def parse():
@@ -94,7 +96,7 @@ def step_flops(w, lens):
 class Model:
     """Per-layer device buffers of one replica of the workload."""
 
-    def __init__(self, w, torch, replicas):
+    def __init__(self, w, torch, replicas, on_chunk=None):
         import fsq_latent_decode_amd as fsq
         self.fsq, self.torch, self.w = fsq, torch, w
         dev = "cuda"
@@ -105,7 +107,7 @@ class Model:
         def bf(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-        fsq_codes = self.fsq_cache(w, torch, bf) if w.codes_from_fsq else None
+        fsq_codes = self.fsq_cache(w, torch, bf, on_chunk) if w.codes_from_fsq else None
         base = []
         for l in range(w.layers):
             E, W = synth.layer_weights(w, l)
@@ -125,21 +127,31 @@ class Model:
         self.ws = fsq.alloc_workspace(w.batch, w.n_q, w.G, self.cap, dev)
         torch.cuda.synchronize()
 
-    def fsq_cache(self, w, torch, bf, chunk=8192):
-        """A cache whose codes are FSQ(E x) (the million-token workload): layer 0's
-        prefill chunks appended through fsq_append, x ~ N(0,1) bf16 drawn per
-        chunk by torch's seeded generator on the device; the layers get copies
-        (timing does not depend on the code values)."""
+    def fsq_cache(self, w, torch, bf, on_chunk=None, chunk=8192):
+        """A cache whose codes are FSQ(E x) (the million-token workload): layer
+        0's prefill chunks appended through fsq_append, x ~ N(0,1) bf16 drawn per
+        chunk from its own seed [workload, 0, T_X, chunk] (synth.layer_x_chunk,
+        generated ahead by host threads); the layers get copies (timing does not
+        depend on the code values). on_chunk(rows, x) sees every chunk's x (the
+        CPU baseline's oracle encodes the same chunks into its own cache)."""
+        from concurrent.futures import ThreadPoolExecutor
         E, _ = synth.layer_weights(w, 0)
         Ed = bf(E)
         codes = torch.empty((w.batch, w.context, w.P), dtype=torch.uint8, device="cuda")
-        g = torch.Generator(device="cuda")
-        g.manual_seed(1_000_003 * w.wid + 7)
-        for b in range(w.batch):
-            for t0 in range(0, w.context, chunk):
-                n = min(chunk, w.context - t0)
-                x = torch.randn((n, w.C), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-                self.fsq.fsq_append(x, Ed, codes[b, t0:t0 + n])
+        n = w.context // chunk
+        assert w.batch == 1 and n * chunk == w.context
+        ahead = 8
+        with ThreadPoolExecutor(ahead) as ex:
+            futs = [ex.submit(synth.layer_x_chunk, w, 0, c, chunk) for c in range(min(ahead, n))]
+            for c in range(n):
+                x = futs[c].result()
+                futs[c] = None
+                if c + ahead < n:
+                    futs.append(ex.submit(synth.layer_x_chunk, w, 0, c + ahead, chunk))
+                rows = slice(c * chunk, (c + 1) * chunk)
+                self.fsq.fsq_append(bf(x), Ed, codes[0, rows])
+                if on_chunk is not None:
+                    on_chunk(rows, x)
         torch.cuda.synchronize()
         return codes
 
@@ -181,11 +193,11 @@ class Model:
                                 workspace=self.ws, split_events=None if ev is None else ev[l])
 
 
-def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False):
+def run_workload(w, torch, steps, warmup, eager, timing_steps, two_call=False, on_chunk=None):
     per_step_bytes = w.layers * (decode_call_bytes(w, synth.seq_lens(w)) + append_call_bytes(w))
     replicas = max(2, math.ceil(4 * MALL_BYTES / per_step_bytes))
     replicas = min(replicas, 8)
-    m = Model(w, torch, replicas)
+    m = Model(w, torch, replicas, on_chunk)
     graphs = None
     if not eager:
         stream = torch.cuda.Stream()
@@ -295,7 +307,8 @@ def append_prefill(w, torch, calls=40, eager=False):
     nbytes = n * w.C * 2 + w.G * w.C * 2 + n * w.P
     flops = 2.0 * n * w.G * w.C
     ach = nbytes / (us * 1e-6) / 1e9
-    return {"workload": w.name, "tokens": n, "C": w.C, "G": w.G, "us_per_call": us,
+    codes0 = codes[0].cpu().numpy()
+    return codes0, {"workload": w.name, "tokens": n, "C": w.C, "G": w.G, "us_per_call": us,
             "tokens_per_s": n / (us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "bytes_per_call": nbytes,
@@ -317,12 +330,35 @@ def copy_probe(torch, mib):
 
 
 # --------------------------------------------------------------- CPU side
-def cpu_baseline(w, seconds, gpu_out=None):
+class OracleCache:
+    """The oracle's own cache of a workload whose codes are FSQ(E x) (the
+    million-token workload): Model.fsq_cache hands it every prefill chunk's x,
+    the oracle encodes it (Eq. 2 and 4 in fp64) into its rows. Only the CPU
+    baseline leg uses it."""
+
+    def __init__(self, w):
+        from oracle import fsq_oracle as orc
+        self.orc, self.w = orc, w
+        E, _ = synth.layer_weights(w, 0)
+        self.Ef = synth.bf16_bits_to_f64(E)
+        self.codes = np.empty((1, w.context, w.P), np.uint8)
+        self.seconds = 0.0
+
+    def __call__(self, rows, x):
+        t = time.perf_counter()
+        self.codes[0, rows] = self.orc.pack_codes(self.orc.encode(synth.bf16_bits_to_f64(x), self.Ef))
+        self.seconds += time.perf_counter() - t
+
+
+def cpu_baseline(w, seconds, gpu_out=None, ref_codes=None, max_layers=None):
     """The fp64 oracle (oracle/) as it stands, on a bounded sample of the step:
     whole layers (one-token append + decode at full context), extrapolated to
     the workload's layer count; timed with the BLAS threads available and with
     one thread. With gpu_out (layer -> the GPU's output of that layer in the
-    timed steps) the oracle's outputs of the sampled layers are compared with it."""
+    timed steps) the oracle's outputs of the sampled layers are compared with
+    it (relative L2 per layer and the worst per head). ref_codes: the oracle's
+    own cache of layer 0 (codes from FSQ(E x), OracleCache); the sample is then
+    that one layer."""
     from oracle import fsq_oracle as orc
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -331,12 +367,15 @@ def cpu_baseline(w, seconds, gpu_out=None):
         threadpool_limits = None
         threads = 1
     lens = synth.seq_lens(w)
+    if ref_codes is not None:
+        max_layers = 1
 
     def inputs(l):
         E, W = synth.layer_weights(w, l)
+        codes = (ref_codes.copy() if ref_codes is not None
+                 else synth.layer_codes(w, l, lens=lens if w.ragged else None))
         return (synth.bf16_bits_to_f64(synth.layer_x(w, l, w.batch, synth.T_XNEW)),
-                synth.bf16_bits_to_f64(synth.layer_query(w, l)),
-                synth.layer_codes(w, l, lens=lens if w.ragged else None),
+                synth.bf16_bits_to_f64(synth.layer_query(w, l)), codes,
                 synth.bf16_bits_to_f64(W), synth.bf16_bits_to_f64(E))
 
     def layer(x, q, packed, Wf, Ef):
@@ -349,7 +388,7 @@ def cpu_baseline(w, seconds, gpu_out=None):
         # layers in order, wrapping to further steps until the time budget is
         # spent (the inputs of a layer are the same in every step)
         done, t_total, outs = 0, 0.0, {}
-        while t_total < budget:
+        while t_total < budget and (max_layers is None or done < max_layers):
             args = inputs(done % w.layers)
             t = time.perf_counter()
             out = layer(*args)
@@ -363,7 +402,7 @@ def cpu_baseline(w, seconds, gpu_out=None):
     per_step = t_total / done * w.layers
     res = {"value": float(np.sum(lens)) / per_step, "unit": "context-tokens/s", "cores": threads,
            "kind": "oracle",
-           "sample": f"{done} layers ({done / w.layers:.2f} steps of {w.layers} layers; one-token append + "
+           "sample": f"{done} layer(s) ({done / w.layers:.2f} steps of {w.layers} layers; one-token append + "
                      f"decode at full context), {t_total:.1f} s of oracle time, scaled to one step",
            "step_s": per_step, "cpu_count": os.cpu_count(),
            "affinity_cores": len(os.sched_getaffinity(0))}
@@ -373,11 +412,52 @@ def cpu_baseline(w, seconds, gpu_out=None):
         res["one_thread"] = {"value": float(np.sum(lens)) / (t1 / d1 * w.layers), "layers": d1,
                              "seconds": t1}
     if gpu_out:
-        errs = [float(np.linalg.norm(gpu_out[l] - outs[l]) / np.linalg.norm(outs[l]))
-                for l in sorted(outs) if l in gpu_out]
+        errs, heads = [], []
+        for l in sorted(outs):
+            if l not in gpu_out:
+                continue
+            g, o = gpu_out[l], outs[l]
+            live = np.asarray(lens) > 0
+            errs.append(float(np.linalg.norm(g - o) / np.linalg.norm(o)))
+            hr = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
+            heads.append(float(hr[live].max()))
         res["parity"] = {"layers": len(errs), "max_rel_l2": max(errs) if errs else None,
-                         "bar": 5e-3, "what": "GPU output of the timed steps vs the oracle, same layers"}
+                         "max_head_rel_l2": max(heads) if heads else None, "bar": 5e-3,
+                         "what": "GPU output of the timed steps vs the oracle, same layers"
+                                 + ("; the oracle decodes its own cache of the same FSQ(E x) chunks"
+                                    if ref_codes is not None else "")}
     return res
+
+
+def cpu_append_baseline(w, gpu_codes, seconds=3.0):
+    """The oracle's encode (Eq. 4 with the Eq. 2 forward value, fp64, then
+    packing) of the workload's prefill chunk, repeated for about `seconds`; its
+    codes are compared with the GPU's append of the same chunk (codes may differ
+    by +-1 only at fp32 rounding ties: the count and largest difference are
+    reported)."""
+    from oracle import fsq_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    n = w.append_tokens
+    E, _ = synth.layer_weights(w, 0)
+    xf = synth.bf16_bits_to_f64(synth.layer_x(w, 0, n))
+    Ef = synth.bf16_bits_to_f64(E)
+    reps, t_total, ref = 0, 0.0, None
+    while t_total < seconds or reps == 0:
+        t = time.perf_counter()
+        ref = orc.encode(xf, Ef)
+        orc.pack_codes(ref)
+        t_total += time.perf_counter() - t
+        reps += 1
+    got = orc.unpack_codes(gpu_codes, w.G)
+    diff = np.abs(got.astype(int) - ref.astype(int))
+    return {"value": n * reps / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} encodes of the {n}-token chunk, {t_total:.1f} s",
+            "parity": {"codes": int(ref.size), "differing": int(np.count_nonzero(diff)),
+                       "max_abs_diff": int(diff.max()), "bar": "at most 1e-4 of codes, each by +-1"}}
 
 
 def split_kernel_bytes(w, lens):
@@ -733,23 +813,38 @@ def main():
         name = next(n for n in [args.workload] + [s for s in args.also.split(",") if s]
                     if synth.WORKLOADS[n].append_tokens)
         print(json.dumps(append_prefill(synth.WORKLOADS[name], torch, calls=12 if args.eager else 40,
-                                        eager=args.eager)))
+                                        eager=args.eager)[1]))
         return
     w = synth.WORKLOADS[args.workload]
+    cpu_on = not args.no_cpu_baseline
+    oracle_caches = {}
+
+    def on_chunk_for(wk):
+        if not (cpu_on and wk.codes_from_fsq and wk.name in CPU_BASELINE_WORKLOADS):
+            return None
+        oracle_caches[wk.name] = OracleCache(wk)
+        return oracle_caches[wk.name]
+
+    def outputs(m, wk):
+        # the GPU's outputs of the timed steps (replica 0), every layer
+        return {l: d["out"].float().cpu().numpy().astype(np.float64) for l, d in enumerate(m.reps[0])}
+
     m, ms, call_ms, reps, step_ms = run_workload(w, torch, args.steps, args.warmup, args.eager,
-                                                 args.timing_steps, args.two_call)
+                                                 args.timing_steps, args.two_call, on_chunk_for(w))
     main_res = summarize(w, ms, call_ms, reps)
     main_res["step_spread"] = step_spread(step_ms)
-    gpu_out = {l: d["out"].float().cpu().numpy().astype(np.float64) for l, d in enumerate(m.reps[0])}
+    gpu_out = outputs(m, w)
     del m
     torch.cuda.empty_cache()
-    also = {}
+    also, also_out = {}, {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
         w2 = synth.WORKLOADS[name]
         m2, ms2, cm2, reps2, sm2 = run_workload(w2, torch, max(5, args.steps // 2), args.warmup,
-                                                args.eager, args.timing_steps, args.two_call)
+                                                args.eager, args.timing_steps, args.two_call, on_chunk_for(w2))
         also[name] = summarize(w2, ms2, cm2, reps2)
         also[name]["step_spread"] = step_spread(sm2)
+        if name in CPU_BASELINE_WORKLOADS:
+            also_out[name] = outputs(m2, w2)
         del m2
         torch.cuda.empty_cache()
     sdpa = {}
@@ -779,9 +874,22 @@ def main():
     app = None
     for name in [args.workload] + [s for s in args.also.split(",") if s]:
         if synth.WORKLOADS[name].append_tokens and not args.no_append:
-            app = append_prefill(synth.WORKLOADS[name], torch)
+            app_codes, app = append_prefill(synth.WORKLOADS[name], torch)
+            if cpu_on:
+                app["cpu_baseline"] = cpu_append_baseline(synth.WORKLOADS[name], app_codes)
             break
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds, gpu_out)
+    cpu = None
+    if cpu_on:
+        oc = oracle_caches.get(w.name)
+        cpu = cpu_baseline(w, args.cpu_seconds, gpu_out, ref_codes=None if oc is None else oc.codes)
+        if oc is not None:
+            cpu["reference_cache_encode_s"] = oc.seconds
+        for name, outs2 in also_out.items():
+            oc = oracle_caches.get(name)
+            also[name]["cpu_baseline"] = cpu_baseline(synth.WORKLOADS[name], args.cpu_seconds * 2 / 3, outs2,
+                                                      ref_codes=None if oc is None else oc.codes)
+            if oc is not None:
+                also[name]["cpu_baseline"]["reference_cache_encode_s"] = oc.seconds
     line = {
         "metric": "decode context-tokens/s",
         "value": main_res["value"],
