@@ -21,9 +21,11 @@
 //                       -> online softmax (exp2) -> MFMA latent pooling ->
 //                       (m, l, zbar fp16); for long chunks decode_stream_kernel
 //                       (below) instead, split on the device for batches
-//   decode_merge_kernel one 16-wave CTA per (sequence, head) (or up to four
+//   decode_merge1_kernel one 16-wave CTA per (sequence, head) (or up to four
 //                       sharing a head's W_v rows): log-sum-exp merge of the
-//                       chunks' zbar, then out = W_v,g zbar
+//                       chunks' zbar by cross-lane reductions, one barrier, then
+//                       out = W_v,g zbar (decode_merge_kernel, two LDS levels,
+//                       when a sequence has more than 4 splits per lane)
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -1778,6 +1780,164 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     if (part == 0 && drow) o[d] = f32_to_bf16(acc);
 }
 
+// Max over the 64 lanes of a wave, in every lane (the pattern of wave_sum_dpp).
+__device__ inline float wave_max_f32(float a) {
+    a = fmaxf(a, dpp_f32<0xB1>(a));
+    a = fmaxf(a, dpp_f32<0x4E>(a));
+    a = fmaxf(a, dpp_f32<0x141>(a));
+    a = fmaxf(a, dpp_f32<0x140>(a));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Sum over the SEG lanes of each SEG-lane segment of a wave (SEG = 64: the
+// whole wave; 32: each half), in every lane of the segment.
+template <int SEG>
+__device__ inline float seg_sum(float a) {
+    if constexpr (SEG == 64) {
+        return wave_sum_dpp(a);
+    } else {
+        static_assert(SEG == 32, "segments of 32 or 64 lanes");
+        a += dpp_f32<0xB1>(a);
+        a += dpp_f32<0x4E>(a);
+        a += dpp_f32<0x141>(a);
+        a += dpp_f32<0x140>(a);
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    }
+}
+
+// Merge with a single barrier. Each SEG-lane segment of a wave merges one
+// 8-coordinate group of the head's partial rows (segment k of wave w: group
+// w 64/SEG + k), its lane l holding splits l, l + SEG, ... (RS of them). Every
+// wave reads the (m, l) pairs of those splits and forms the common max M by a
+// wave-wide reduction in registers, the weights c_s = l_s 2^(m_s - M) and
+// L = sum_s c_s by segment reductions; then zbar = sum_s c_s zbar_s / L per
+// coordinate, reduced the same way, goes to LDS. After the one barrier,
+// out = W_v,g zbar as in the two-level kernel (same W_v rows per CTA).
+template <int VW, int RS, int SEG>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
+    const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
+    const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
+    uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
+    int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta, MergeGeom geo) {
+    using VT = typename VecT<VW>::T;
+    constexpr int NVA = (kMaxG / VW + 3) / 4;
+    constexpr int NVR = VW >= 4 ? 8 : 16;
+    constexpr int NVT = NVA < NVR ? NVA : NVR;
+    constexpr int NSEG = 64 / SEG;
+    __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sl = lane % SEG;
+    const int kg = wave * NSEG + lane / SEG;   // this lane's coordinate group
+    const int DR = geo.DR, d0 = (int)blockIdx.z * DR;
+    uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
+    const int32_t T_raw = seq_lens[b];
+    const int32_t tl_raw = dyn_batch > 1 && lane < dyn_batch ? seq_lens[lane] : 0;
+    // ---- issue: W_v row d, vectors part, part + TPR, ... (the coldest data)
+    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
+    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
+    const int TPR = 1 << geo.tpr_log2;
+    const int NV = G / VW;
+    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
+    const bool drow = (tid >> geo.tpr_log2) < DR;
+    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
+    VT wv[NVT];
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+        const int vi = part + TPR * i;
+        if (vi < NV) wv[i] = wrow[vi];
+    }
+    int chunk = chunk_arg, s_rows = S;
+    if (dyn_batch > 0) {
+        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
+        const int64_t tl = tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
+        const int nsb = (int)(((uint32_t)tb + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // tb < 2^31
+        s_rows = nsb < 1 ? 1 : nsb;
+    }
+    // ---- issue: this lane's (m, l) pairs and partial rows (indices clamped;
+    // entries of splits at or past the sequence's split count are selected out)
+    const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + ((size_t)b * n_q + h) * S;
+    const _Float16 *zp = part_z + ((size_t)b * n_q + h) * S * GP;
+    const int KG = GP / 8;
+    const int kgc = kg < KG ? kg : 0;
+    float2 mr[RS];
+    half8 v[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+        const int sidx = sl + SEG * i, sc = sidx < s_rows ? sidx : 0;
+        mr[i] = ml[sc];
+        v[i] = *reinterpret_cast<const half8 *>(zp + (size_t)sc * GP + kgc * 8);
+    }
+    const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
+    const int ns = (int)((T + (uint32_t)chunk - 1u) / (uint32_t)chunk);
+    if (ns == 0) {   // empty sequence (uniform): the output is zero
+        for (int dd = tid; dd < DR; dd += kMergeThreads) o[d0 + dd] = 0;
+        return;
+    }
+    // ---- common max, weights and normaliser (the same bits in every wave)
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+        if (sl + SEG * i < ns) m = fmaxf(m, mr[i].x);
+    m = wave_max_f32(m);   // finite: split 0 is in every sequence with ns > 0
+    float c[RS], l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+        // rows past the sequence's splits hold stale workspace contents (possibly
+        // not finite): selected out, not multiplied by 0
+        c[i] = sl + SEG * i < ns ? mr[i].y * __builtin_amdgcn_exp2f(mr[i].x - m) : 0.0f;
+        l += c[i];
+    }
+    l = seg_sum<SEG>(l);
+    const float inv = 1.0f / l;
+    // ---- this segment's coordinate group
+    float a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+        const bool ok = sl + SEG * i < ns;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] += ok ? c[i] * (float)v[i][j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = seg_sum<SEG>(a[j]);
+    if (sl == 0 && kg < KG) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int pp = kg * 8 + j;
+            zbar[natural ? pp : pos_to_coord(pp, GP, bits)] = a[j] * inv;
+        }
+    }
+    __syncthreads();
+    // ---- out = W_v,g zbar
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+        const int vi = part + TPR * i;
+        float wf[VW];
+        bf16_vec_to_f32<VW>(wv[i], wf);
+        if (vi < NV) {
+#pragma unroll
+            for (int cc = 0; cc < VW; ++cc) acc += wf[cc] * zbar[vi * VW + cc];
+        }
+    }
+    for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
+        float wf[VW];
+        bf16_vec_to_f32<VW>(wrow[vi], wf);
+#pragma unroll
+        for (int cc = 0; cc < VW; ++cc) acc += wf[cc] * zbar[vi * VW + cc];
+    }
+    for (int off = TPR >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == 0 && drow) o[d] = f32_to_bf16(acc);
+}
+
 // Merge launch: the widest bf16 vector that divides G and the W_kv alignment,
 // and the fewest partial rows per thread that cover S in one batch (at most 8).
 static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint16_t *W_kv,
@@ -1808,6 +1968,31 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
     geo.ZS = GP + (geo.tpp_log2 == 5 ? 4 : 64 >> geo.tpp_log2);
     const int grp = n_q / n_kv;
     geo.g_mul = ((1 << 20) + grp - 1) / grp;
+    // the one-barrier merge: one coordinate group per 64-lane wave (widths up to
+    // 128) or per 32-lane half (up to 256), at most 4 splits per lane; more
+    // splits (long single sequences) take the two-level kernel
+    const int seg = GP <= 128 ? 64 : 32;
+    const int rs = (S + seg - 1) / seg;
+    if (rs <= 4) {
+        const int rs2 = rs <= 1 ? 1 : rs <= 2 ? 2 : 4;
+#define FSQ_MERGE1_CASE(VWX, RSX, SEGX)                                                                    \
+    if (vw == VWX && rs2 == RSX && seg == SEGX) {                                                         \
+        decode_merge1_kernel<VWX, RSX, SEGX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out,  \
+                                                                           seq_cap, G, GP, n_q, n_kv, d_h, \
+                                                                           chunk, S, natural, bits,       \
+                                                                           dyn_batch, ncta, geo);         \
+        return hipGetLastError();                                                                         \
+    }
+#define FSQ_MERGE1_VW(VWX)                                                                                \
+    FSQ_MERGE1_CASE(VWX, 1, 64) FSQ_MERGE1_CASE(VWX, 2, 64) FSQ_MERGE1_CASE(VWX, 4, 64)                   \
+    FSQ_MERGE1_CASE(VWX, 1, 32) FSQ_MERGE1_CASE(VWX, 2, 32) FSQ_MERGE1_CASE(VWX, 4, 32)
+        FSQ_MERGE1_VW(8)
+        FSQ_MERGE1_VW(4)
+        FSQ_MERGE1_VW(2)
+        FSQ_MERGE1_VW(1)
+#undef FSQ_MERGE1_VW
+#undef FSQ_MERGE1_CASE
+    }
 #define FSQ_MERGE_CASE(VWX, RX)                                                                           \
     if (vw == VWX && r == RX) {                                                                           \
         decode_merge_kernel<VWX, RX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out, seq_cap, \
