@@ -498,6 +498,23 @@ def _profile_bytes(path, files):
         return None
 
 
+def graph_replayed_split_us(w):
+    """The split-K kernel's average duration over graph-replayed launches, from
+    the committed rocprofv3 kernel trace of the same sources (HIP events cannot
+    be recorded inside a captured graph, so the live measurement is eager)."""
+    for f in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not f.startswith("decode_step_kernels_"):
+            continue
+        kv = {}
+        for line in open(os.path.join(ROOT, "profiles", f)):
+            if "=" in line and not line.startswith(("#", "|")):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_src_sha256") == kernel_src_sha(DECODE_SRC) and f"split_k_graph_avg_us.{w.name}" in kv:
+            return float(kv[f"split_k_graph_avg_us.{w.name}"]), f
+    return None, None
+
+
 def traffic_from_profile(w):
     """HBM bytes per split-K launch from the committed counter summary."""
     return _profile_bytes(os.path.join(ROOT, "profiles", f"decode_split_traffic_{w.name}.txt"), DECODE_SRC)
@@ -796,6 +813,13 @@ def summarize(w, ms, call_ms, replicas):
                            "kernel": plan["kernel"], **split, "bytes_per_launch": nbytes,
                            "avg_launch_us": avg * 1e3, "launches_timed": len(call_ms),
                            "timing": "hipExtLaunchKernelGGL start/stop events, eager steps"}
+        g_us, g_src = graph_replayed_split_us(w)
+        if g_us is not None:
+            g_ach = nbytes / (g_us * 1e-6) / 1e9
+            res["roofline"]["graph_replayed"] = {"avg_launch_us": g_us, "achieved": g_ach,
+                                                 "frac": g_ach / HBM_PEAK_GBS,
+                                                 "timing": f"rocprofv3 kernel trace of the graph-replayed steps "
+                                                           f"(profiles/{g_src}), same sources"}
     return res
 
 
