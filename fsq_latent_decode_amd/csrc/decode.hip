@@ -412,14 +412,18 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     // ---- per-lane loads of one tile (this lane's half of token t)
     uint32_t ld[NLD];
     int ld_ntok = 0, ld_sh = 0;
+    // Every load is unconditional (tiles past the chunk re-read its first row,
+    // and are never used), so that a wait for one load counts exactly the loads
+    // issued after it.
     auto issue = [&](int64_t t0) {
         const int64_t rem = c1 - t0;
         ld_ntok = rem <= 0 ? 0 : (rem < kTile ? (int)rem : kTile);
-        if (ld_ntok == 0) return;
-        const int tc = t < ld_ntok ? t : ld_ntok - 1;
+        const int64_t tb = ld_ntok == 0 ? c0 : t0;
+        const int nr = ld_ntok == 0 ? 1 : ld_ntok;
+        const int tc = t < nr ? t : nr - 1;
         if (AL) {
             // G == GP and P % 16 == 0: the half is ND whole, 8-byte aligned dwords
-            const uint2 *src = reinterpret_cast<const uint2 *>(seq + (size_t)(t0 + tc) * P + hh * HB);
+            const uint2 *src = reinterpret_cast<const uint2 *>(seq + (size_t)(tb + tc) * P + hh * HB);
 #pragma unroll
             for (int i = 0; i < ND / 2; ++i) {
                 const uint2 v = src[i];
@@ -428,56 +432,70 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
             }
         } else {
             // aligned dwords around the half, clamped to the tile's last dword
-            const uint8_t *a = seq + (size_t)(t0 + tc) * P + hh * HB;
+            const uint8_t *a = seq + (size_t)(tb + tc) * P + hh * HB;
             ld_sh = (int)((uintptr_t)a & 3) * 8;
             const uint32_t *a0 = reinterpret_cast<const uint32_t *>(a - ((uintptr_t)a & 3));
-            const uint8_t *lastb = seq + (size_t)(t0 + ld_ntok) * P - 1;
+            const uint8_t *lastb = seq + (size_t)(tb + nr) * P - 1;
             const uint32_t *last = reinterpret_cast<const uint32_t *>(lastb - ((uintptr_t)lastb & 3));
 #pragma unroll
             for (int i = 0; i < NLD; ++i) ld[i] = *(a0 + i <= last ? a0 + i : last);
         }
     };
 
-    issue(c0 + wave * kTile);
-
     // Q~ rows of this head group (32 x GP fp16, contiguous) are read from global
     // once per CTA into LDS (rows padded to GP + 8 halves for conflict-free
-    // 16-byte reads), then each wave takes its B operands from there
+    // 16-byte reads), then each wave takes its B operands from there. They are
+    // requested first, so that staging them waits for them alone while the
+    // first tile's codes are still in flight.
+    constexpr int NQ16 = 32 * GP / 8;                    // 16-byte chunks
+    constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
+    u32x4 qreg[NQI];
+    {
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
+#pragma unroll
+        for (int u = 0; u < NQI; ++u) {
+            const int i = threadIdx.x + u * NW * 64;
+            qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
+        }
+    }
     half8 qv[KB];
     // 8-bit codes: the residual term of q~ (see absorb_rows), B operands read
-    // straight from global memory, issued with the first tile's loads
+    // straight from global memory
     half8 qvl[BITS == 8 ? KB : 1];
     if constexpr (BITS == 8) {
         const _Float16 *ql = qt + qlo + ((size_t)b * nqp + hg * 32 + t) * GP + 8 * hh;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) qvl[kb] = *reinterpret_cast<const half8 *>(ql + 16 * kb);
     }
+    // issue order pinned: Q~, then the first tile (the compiler would move the
+    // tile's loads behind the Q~ barrier, or ahead of the Q~ loads)
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c0 + wave * kTile);
+    __builtin_amdgcn_sched_barrier(0);
+
     {
         constexpr int QROW = GP + 8;
         _Float16 *qsm = reinterpret_cast<_Float16 *>(psm);   // free until the first max barrier
-        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(qt + ((size_t)b * nqp + hg * 32) * GP);
-        constexpr int NQ16 = 32 * GP / 8;                    // 16-byte chunks
-        constexpr int NQI = (NQ16 + NW * 64 - 1) / (NW * 64);
-        // every load is issued before the first LDS write (clamped index, guarded store)
-        u32x4 qreg[NQI];
 #pragma unroll
         for (int u = 0; u < NQI; ++u) {
-            const int i = threadIdx.x + u * NW * 64;
-            qreg[u] = qsrc[i < NQ16 ? i : NQ16 - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < NQI; ++u) {
-            const int i = threadIdx.x + u * NW * 64;
+            // threads past the last chunk rewrite it with the same data (no
+            // branch, so that its load stays where it was issued)
+            const int i0 = threadIdx.x + u * NW * 64, i = i0 < NQ16 ? i0 : NQ16 - 1;
             const int r = i / (GP / 8), c = i - r * (GP / 8);
-            if (NQ16 % (NW * 64) == 0 || i < NQ16)
-                *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
+            *reinterpret_cast<u32x4 *>(qsm + r * QROW + 8 * c) = qreg[u];
         }
         __syncthreads();
         // the sequence length: leave if this chunk is past it (uniform), else
         // bound the chunk and recount the first round's tokens
         int64_t T = T_raw;
         T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
-        if (c0 >= T) return;
+        if (c0 >= T) {
+            // the first tile's words are used on this path too (waited for,
+            // harmlessly, before leaving), so that their loads stay ahead of
+            // the Q~ barrier instead of being sunk behind this branch
+            asm volatile("" ::"v"(ld[0]));
+            return;
+        }
         c1 = (c0 + chunk < T) ? c0 + chunk : T;
         const int64_t rem0 = c1 - (c0 + wave * kTile);
         ld_ntok = rem0 <= 0 ? 0 : (rem0 < kTile ? (int)rem0 : kTile);
@@ -1817,16 +1835,13 @@ __device__ inline float seg_sum(float a) {
 // L = sum_s c_s by segment reductions; then zbar = sum_s c_s zbar_s / L per
 // coordinate, reduced the same way, goes to LDS. After the one barrier,
 // out = W_v,g zbar as in the two-level kernel (same W_v rows per CTA).
-template <int VW, int RS, int SEG>
+template <int VW, int RS, int SEG, int NVW>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
     int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta, MergeGeom geo) {
     using VT = typename VecT<VW>::T;
-    constexpr int NVA = (kMaxG / VW + 3) / 4;
-    constexpr int NVR = VW >= 4 ? 8 : 16;
-    constexpr int NVT = NVA < NVR ? NVA : NVR;
     constexpr int NSEG = 64 / SEG;
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
     const int h = blockIdx.x, b = blockIdx.y;
@@ -1836,32 +1851,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     const int kg = wave * NSEG + lane / SEG;   // this lane's coordinate group
     const int DR = geo.DR, d0 = (int)blockIdx.z * DR;
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
-    const int32_t T_raw = seq_lens[b];
-    const int32_t tl_raw = dyn_batch > 1 && lane < dyn_batch ? seq_lens[lane] : 0;
-    // ---- issue: W_v row d, vectors part, part + TPR, ... (the coldest data)
-    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
-    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
-    const int TPR = 1 << geo.tpr_log2;
-    const int NV = G / VW;
-    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
-    const bool drow = (tid >> geo.tpr_log2) < DR;
-    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
-    VT wv[NVT];
-#pragma unroll
-    for (int i = 0; i < NVT; ++i) {
-        const int vi = part + TPR * i;
-        if (vi < NV) wv[i] = wrow[vi];
-    }
-    int chunk = chunk_arg, s_rows = S;
-    if (dyn_batch > 0) {
-        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
-        const int64_t tl = tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
-        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
-        const int nsb = (int)(((uint32_t)tb + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // tb < 2^31
-        s_rows = nsb < 1 ? 1 : nsb;
-    }
-    // ---- issue: this lane's (m, l) pairs and partial rows (indices clamped;
-    // entries of splits at or past the sequence's split count are selected out)
+    // ---- loads, all unconditional (clamped indices), so that a wait for one
+    // counts exactly the loads issued after it: the batch's lengths (device-side
+    // split of a batch), this lane's (m, l) pairs and partial rows (bounded by
+    // the workspace's S rows, not by the sequence length, which is not known
+    // yet), then the W_v rows, which are used last and stay in flight meanwhile
+    const int32_t tl_raw = seq_lens[min(lane, (dyn_batch > 1 ? dyn_batch : 1) - 1)];
     const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + ((size_t)b * n_q + h) * S;
     const _Float16 *zp = part_z + ((size_t)b * n_q + h) * S * GP;
     const int KG = GP / 8;
@@ -1870,9 +1865,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     half8 v[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
-        const int sidx = sl + SEG * i, sc = sidx < s_rows ? sidx : 0;
+        const int sc = min(sl + SEG * i, S - 1);
         mr[i] = ml[sc];
         v[i] = *reinterpret_cast<const half8 *>(zp + (size_t)sc * GP + kgc * 8);
+    }
+    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
+    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
+    const int TPR = 1 << geo.tpr_log2;
+    const int NV = G / VW;
+    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
+    const bool drow = (tid >> geo.tpr_log2) < DR;
+    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
+    VT wv[NVW];
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) wv[i] = wrow[min(part + TPR * i, NV - 1)];
+    // ---- the sequence's split count
+    const int32_t T_raw = seq_lens[b];
+    int chunk = chunk_arg;
+    if (dyn_batch > 0) {
+        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
+        const int64_t tl = lane >= dyn_batch || tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
     }
     const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
     const int ns = (int)((T + (uint32_t)chunk - 1u) / (uint32_t)chunk);
@@ -1883,8 +1896,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     // ---- common max, weights and normaliser (the same bits in every wave)
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < RS; ++i)
-        if (sl + SEG * i < ns) m = fmaxf(m, mr[i].x);
+    for (int i = 0; i < RS; ++i) m = fmaxf(m, sl + SEG * i < ns ? mr[i].x : -INFINITY);
     m = wave_max_f32(m);   // finite: split 0 is in every sequence with ns > 0
     float c[RS], l = 0.0f;
 #pragma unroll
@@ -1916,10 +1928,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
         }
     }
     __syncthreads();
-    // ---- out = W_v,g zbar
+    // ---- out = W_v,g zbar (vectors part + TPR i; past NVW of them, read here)
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NVT; ++i) {
+    for (int i = 0; i < NVW; ++i) {
         const int vi = part + TPR * i;
         float wf[VW];
         bf16_vec_to_f32<VW>(wv[i], wf);
@@ -1928,7 +1940,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
             for (int cc = 0; cc < VW; ++cc) acc += wf[cc] * zbar[vi * VW + cc];
         }
     }
-    for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
+    for (int vi = part + TPR * NVW; vi < NV; vi += TPR) {
         float wf[VW];
         bf16_vec_to_f32<VW>(wrow[vi], wf);
 #pragma unroll
@@ -1975,22 +1987,26 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
     const int rs = (S + seg - 1) / seg;
     if (rs <= 4) {
         const int rs2 = rs <= 1 ? 1 : rs <= 2 ? 2 : 4;
-#define FSQ_MERGE1_CASE(VWX, RSX, SEGX)                                                                    \
-    if (vw == VWX && rs2 == RSX && seg == SEGX) {                                                         \
-        decode_merge1_kernel<VWX, RSX, SEGX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out,  \
-                                                                           seq_cap, G, GP, n_q, n_kv, d_h, \
-                                                                           chunk, S, natural, bits,       \
-                                                                           dyn_batch, ncta, geo);         \
-        return hipGetLastError();                                                                         \
+        const int nv = G / vw, tpr = 1 << geo.tpr_log2;
+        const int nvw_need = (nv + tpr - 1) / tpr;
+        const int nvw = nvw_need <= 1 ? 1 : nvw_need <= 2 ? 2 : 4;   // more: read in the dot loop
+#define FSQ_MERGE1_CASE(VWX, RSX, SEGX, NVWX)                                                               \
+    if (vw == VWX && rs2 == RSX && seg == SEGX && nvw == NVWX) {                                           \
+        decode_merge1_kernel<VWX, RSX, SEGX, NVWX><<<mg, kMergeThreads, 0, st>>>(                          \
+            pz, pml, W_kv, seq_lens, out, seq_cap, G, GP, n_q, n_kv, d_h, chunk, S, natural, bits,         \
+            dyn_batch, ncta, geo);                                                                         \
+        return hipGetLastError();                                                                          \
     }
-#define FSQ_MERGE1_VW(VWX)                                                                                \
-    FSQ_MERGE1_CASE(VWX, 1, 64) FSQ_MERGE1_CASE(VWX, 2, 64) FSQ_MERGE1_CASE(VWX, 4, 64)                   \
-    FSQ_MERGE1_CASE(VWX, 1, 32) FSQ_MERGE1_CASE(VWX, 2, 32) FSQ_MERGE1_CASE(VWX, 4, 32)
+#define FSQ_MERGE1_RS(VWX, NVWX)                                                                           \
+    FSQ_MERGE1_CASE(VWX, 1, 64, NVWX) FSQ_MERGE1_CASE(VWX, 2, 64, NVWX) FSQ_MERGE1_CASE(VWX, 4, 64, NVWX)  \
+    FSQ_MERGE1_CASE(VWX, 1, 32, NVWX) FSQ_MERGE1_CASE(VWX, 2, 32, NVWX) FSQ_MERGE1_CASE(VWX, 4, 32, NVWX)
+#define FSQ_MERGE1_VW(VWX) FSQ_MERGE1_RS(VWX, 1) FSQ_MERGE1_RS(VWX, 2) FSQ_MERGE1_RS(VWX, 4)
         FSQ_MERGE1_VW(8)
         FSQ_MERGE1_VW(4)
         FSQ_MERGE1_VW(2)
         FSQ_MERGE1_VW(1)
 #undef FSQ_MERGE1_VW
+#undef FSQ_MERGE1_RS
 #undef FSQ_MERGE1_CASE
     }
 #define FSQ_MERGE_CASE(VWX, RX)                                                                           \
