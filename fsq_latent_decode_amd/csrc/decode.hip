@@ -1606,19 +1606,13 @@ struct MergeGeom {
 };
 constexpr int kMergeMaxS = 1024;
 
-template <int VW, int R>
+template <int VW, int R, int NVW>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const _Float16 *__restrict__ part_z, const float *__restrict__ part_ml,
     const uint16_t *__restrict__ W_kv, const int32_t *__restrict__ seq_lens,
     uint16_t *__restrict__ out, int64_t seq_cap, int G, int GP, int n_q, int n_kv, int d_h,
     int chunk_arg, int S, int natural, int bits, int dyn_batch, int ncta, MergeGeom geo) {
     using VT = typename VecT<VW>::T;
-    // W_v vectors per thread: a row is shared by TPR >= 4 threads (d_h <= 256),
-    // so at most NVA per thread; NVT of them (at most 32 VGPRs) are held from the
-    // start, the rest (narrow vectors only) are read in the dot loop
-    constexpr int NVA = (kMaxG / VW + 3) / 4;
-    constexpr int NVR = VW >= 4 ? 8 : 16;
-    constexpr int NVT = NVA < NVR ? NVA : NVR;
     __shared__ __attribute__((aligned(16))) float zpart[9216];   // [split group][ZS]: ZS * SG <= 9216
     __shared__ float gm[256], gl[256];                            // per split group: SG <= 256
     __shared__ __attribute__((aligned(16))) float zbar[kMaxG];
@@ -1627,39 +1621,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int DR = geo.DR, d0 = (int)blockIdx.z * DR;   // this CTA's rows of W_v
     uint16_t *o = out + ((size_t)b * n_q + h) * d_h;
     const size_t srow = 1;   // rows between splits (head-major partials)
-    // The sequence length is read first; the loads below are issued over all S
-    // splits of the workspace (indices clamped) before it arrives, and entries
-    // of splits at or past the sequence's split count ns are discarded by selects.
-    const int32_t T_raw = seq_lens[b];
-    // device-side split: every length, one per lane, ahead of the W_v loads so
-    // that waiting for them does not wait for W_v
-    const int32_t tl_raw = dyn_batch > 1 && (tid & 63) < dyn_batch ? seq_lens[tid & 63] : 0;
-    // ---- issue: W_v row d, vectors part, part + TPR, ... (first: W_v is the
-    // coldest data, read from HBM, while the partials were just written)
-    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
-    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
-    const int TPR = 1 << geo.tpr_log2;
-    const int NV = G / VW;
-    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
-    const bool drow = (tid >> geo.tpr_log2) < DR;
-    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
-    VT wv[NVT];
-#pragma unroll
-    for (int i = 0; i < NVT; ++i) {
-        const int vi = part + TPR * i;
-        if (vi < NV) wv[i] = wrow[vi];   // others unused
-    }
-    // the chunk of the split kernel: the plan's, or the device-side split's (which
-    // also bounds the rows worth reading: the sequence's split count)
-    int chunk = chunk_arg, s_rows = S;
-    if (dyn_batch > 0) {
-        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
-        const int64_t tl = tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
-        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
-        const int nsb = (int)(((uint32_t)tb + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // tb < 2^31
-        s_rows = nsb < 1 ? 1 : nsb;
-    }
-    // ---- issue: partial rows sg + u SG and their (m, l)
+    // ---- loads, all unconditional (clamped indices), so that a wait for one
+    // counts exactly the loads issued after it: the batch's lengths (device-side
+    // split of a batch), the first R partial rows of this thread and their
+    // (m, l) over the workspace's S splits (entries at or past the sequence's
+    // split count ns are discarded by selects once it is known), then the W_v
+    // rows, which are used last and stay in flight meanwhile
+    const int32_t tl_raw = seq_lens[min(tid & 63, (dyn_batch > 1 ? dyn_batch : 1) - 1)];
     const int KG = geo.KG, SG = geo.SG;
     // level 2 uses TPP threads per position; zpart rows are padded to ZS floats,
     // ZS = 64 / TPP (mod 32), so a wave's 64 reads fall on distinct bank pairs
@@ -1673,9 +1641,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     float2 mr[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        const int i = sg + u * SG, ic = zthr && i < s_rows ? i : 0;
+        const int ic = min(sg + u * SG, S - 1);
         v[u] = *reinterpret_cast<const half8 *>(zp + (size_t)ic * srow * GP);
         mr[u] = ml[(size_t)ic * srow];
+    }
+    const int g = (int)(((uint32_t)h * (uint32_t)geo.g_mul) >> 20);
+    const uint16_t *Wv = W_kv + ((size_t)n_kv * d_h + (size_t)g * d_h) * G;
+    const int TPR = 1 << geo.tpr_log2;
+    const int NV = G / VW;
+    const int d = d0 + (tid >> geo.tpr_log2), part = tid & (TPR - 1);
+    const bool drow = (tid >> geo.tpr_log2) < DR;
+    const VT *wrow = reinterpret_cast<const VT *>(Wv + (size_t)(drow ? d : 0) * G);
+    VT wv[NVW];
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) wv[i] = wrow[min(part + TPR * i, NV - 1)];
+    // the chunk of the split kernel: the plan's, or the device-side split's
+    const int32_t T_raw = seq_lens[b];
+    int chunk = chunk_arg;
+    if (dyn_batch > 0) {
+        const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
+        const int64_t tl = (tid & 63) >= dyn_batch || tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
     }
     // T < 2^31 and chunk < 2^30: the split count in 32-bit arithmetic
     const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
@@ -1779,7 +1765,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     // ---- out = W_v,g zbar
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NVT; ++i) {
+    for (int i = 0; i < NVW; ++i) {
         const int vi = part + TPR * i;
         float wf[VW];
         bf16_vec_to_f32<VW>(wv[i], wf);
@@ -1788,7 +1774,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
             for (int c = 0; c < VW; ++c) acc += wf[c] * zbar[vi * VW + c];
         }
     }
-    for (int vi = part + TPR * NVT; vi < NV; vi += TPR) {
+    for (int vi = part + TPR * NVW; vi < NV; vi += TPR) {
         float wf[VW];
         bf16_vec_to_f32<VW>(wrow[vi], wf);
 #pragma unroll
@@ -2009,19 +1995,25 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
 #undef FSQ_MERGE1_RS
 #undef FSQ_MERGE1_CASE
     }
-#define FSQ_MERGE_CASE(VWX, RX)                                                                           \
-    if (vw == VWX && r == RX) {                                                                           \
-        decode_merge_kernel<VWX, RX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out, seq_cap, \
-                                                                   G, GP, n_q, n_kv, d_h, chunk, S,       \
-                                                                   natural, bits, dyn_batch, ncta, geo);  \
+    const int nv2 = G / vw, tpr2 = 1 << geo.tpr_log2;
+    const int nvw2_need = (nv2 + tpr2 - 1) / tpr2;
+    const int nvw2 = nvw2_need <= 1 ? 1 : nvw2_need <= 2 ? 2 : 4;   // more: read in the dot loop
+#define FSQ_MERGE_CASE(VWX, RX, NVWX)                                                                      \
+    if (vw == VWX && r == RX && nvw2 == NVWX) {                                                           \
+        decode_merge_kernel<VWX, RX, NVWX><<<mg, kMergeThreads, 0, st>>>(pz, pml, W_kv, seq_lens, out,    \
+                                                                         seq_cap, G, GP, n_q, n_kv, d_h,  \
+                                                                         chunk, S, natural, bits,         \
+                                                                         dyn_batch, ncta, geo);           \
         return hipGetLastError();                                                                         \
     }
-#define FSQ_MERGE_VW(VWX) FSQ_MERGE_CASE(VWX, 2) FSQ_MERGE_CASE(VWX, 4) FSQ_MERGE_CASE(VWX, 8)
+#define FSQ_MERGE_R(VWX, NVWX) FSQ_MERGE_CASE(VWX, 2, NVWX) FSQ_MERGE_CASE(VWX, 4, NVWX) FSQ_MERGE_CASE(VWX, 8, NVWX)
+#define FSQ_MERGE_VW(VWX) FSQ_MERGE_R(VWX, 1) FSQ_MERGE_R(VWX, 2) FSQ_MERGE_R(VWX, 4)
     FSQ_MERGE_VW(8)
     FSQ_MERGE_VW(4)
     FSQ_MERGE_VW(2)
     FSQ_MERGE_VW(1)
 #undef FSQ_MERGE_VW
+#undef FSQ_MERGE_R
 #undef FSQ_MERGE_CASE
     return hipErrorInvalidValue;
 }
