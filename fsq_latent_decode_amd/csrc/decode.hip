@@ -102,6 +102,38 @@ __device__ inline half8 unpack_codes_x16(uint32_t w) {
     return __builtin_bit_cast(half8, t);
 }
 
+// The same operands as unpack_codes_x16, but as normal fp16 numbers 1024 + n
+// (1024 + 16 n at the odd positions): the nibbles are placed under the
+// exponent of 1024 by an AND-OR, as cheap as the AND. Against q~ this adds
+// 1024 sum_k q~_k to every score of a head, a constant that cancels in the
+// softmax and in the merge of splits; in exchange the product is in log2 units
+// already (no 2^24 scale before the exponential).
+// v_and_or_b32 takes no literal operands on this target, so the three
+// constants live in VGPRs (kept there across the tile loop); without the asm
+// the compiler emits a separate AND and OR per operand dword.
+// (an instruction may read one scalar register: the masks are in scalar
+// registers, the exponent bits in a vector register)
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+    return r;
+}
+struct X16nConst {
+    uint32_t lo, hi, e;
+};
+__device__ inline X16nConst x16n_const() {
+    // opaque to the compiler, so the values stay in registers instead of being
+    // re-materialised as literals next to every use
+    X16nConst c{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+s"(c.lo), "+s"(c.hi), "+v"(c.e));
+    return c;
+}
+__device__ inline half8 unpack_codes_x16n(uint32_t w, const X16nConst &c) {
+    const uint32_t w8 = w >> 8;
+    const u32x4 t = {and_or(w, c.lo, c.e), and_or(w, c.hi, c.e), and_or(w8, c.lo, c.e), and_or(w8, c.hi, c.e)};
+    return __builtin_bit_cast(half8, t);
+}
+
 // Row of token r (0..31) in the nibble tile: the 16 tokens a transposed read
 // gathers for one lane half are rows 16 hh .. 16 hh + 15.
 __device__ inline int tile_row(int r) { return ((r >> 3) << 2) | (r & 3) | (((r >> 2) & 1) << 4); }
@@ -1024,7 +1056,7 @@ __device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int 
 }
 
 template <int GP, int NW, int D, bool AL, int RC>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : (GP >= 128 ? 2 : 3)))) void decode_stream_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 : 2))) void decode_stream_kernel(
     const _Float16 *__restrict__ qt, const uint8_t *__restrict__ codes,
     const int32_t *__restrict__ seq_lens, _Float16 *__restrict__ part_z,
     float *__restrict__ part_ml, int64_t seq_cap, int G, int n_q, int nqp, int chunk_arg, int S,
@@ -1037,6 +1069,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // scores arrive in units of 2^-24 from absorbed queries (codes as fp16
     // subnormals), in plain log2 units from rebuilt keys (rescaled below)
     constexpr float kSS = RC ? 1.0f : kCodeScale;
+    // absorbed queries below GP 128: scores computed in the wave's frame (see
+    // weigh); wider latents keep the running max (no registers to spare for
+    // the frame's constants, whose spills cost more than they save)
+    constexpr bool FRAME = !RC && GP < 128;
     constexpr int WROW = GP + 8;   // rebuilt-key operand rows (halves), RC only
     // s_waitcnt immediates (gfx9 layout), only vmcnt waited on
     constexpr int kWaitAhead = (((D - 1) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 1) * NI) >> 4) << 14);
@@ -1148,12 +1184,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         }
     };
 
+    // Below GP 128 (absorbed queries) the codes bypass the ring: each lane loads
+    // the dwords around its half of its token's row straight into registers,
+    // four tiles ahead (REG below); the ring and its LDS reads serve the wider
+    // latents and the key-reconstruction variants.
+    constexpr bool REG = C::PAIR && !RC;
+    // dwords per lane and tile (REG): the KB + 1 aligned dwords around the
+    // lane's half (funnel-shifted by its byte offset) for every row alignment
+    constexpr int NLD = KB + 1;
+    // lane window: byte loff of the 4-byte aligned sequence base sb, relative to
+    // each tile's first row (t0 P is a multiple of 4: t0 is a multiple of 32)
+    const uint32_t loff = (uint32_t)(((uintptr_t)seq & 3u) + (uint32_t)(t * P + hh * (GP / 4)));
+    const uint32_t voff = loff & ~3u, fsh = (loff & 3u) * 8u;
+    // (pointer arithmetic rather than integer casts, so that the compiler keeps
+    // these global-memory pointers and emits global, not flat, loads)
+    const uint8_t *sb = seq - ((uintptr_t)seq & 3u);
+    // the last dword holding bytes of this sequence's rows (clamp of the tiles
+    // that end near the cache capacity)
+    const uint8_t *lastb = seq + (size_t)seq_cap * P - 1;
+    const uint8_t *lastdw = lastb - ((uintptr_t)lastb & 3u);
+    uint32_t rb[REG ? 4 : 1][REG ? NLD : 1];
+    // tile jt of this wave into registers. The loads need no bounds checks
+    // while the windows end inside the next row (t0 + 32 < seq_cap); a tile
+    // past the chunk, or the one tile that ends at the cache capacity, loads
+    // the sequence's first tile instead (a valid address; that data is never
+    // used: the capacity-end tile is reloaded with clamped addresses when it
+    // is processed). The plan takes this kernel only for seq_cap >= 64.
+    auto load_tile = [&](int jt, auto &dst) {
+        if constexpr (REG) {
+            int64_t t0 = tile_t0(jt);
+            if (t0 >= cend || t0 + kTile >= seq_cap) t0 = 0;
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(sb + (size_t)t0 * P + voff);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) dst[i] = src[i];
+        }
+    };
     // Q~ rows of this head group -> LDS (rows padded to GP + 8 halves) -> each
     // lane's B operands, as in the split kernel. Only the first tile is loaded
     // alongside (the compiler waits for all loads before the Q~ stores); the
     // ring's other D - 2 tiles are issued once Q~ is in place, so they are in
-    // flight while the first tile is processed.
-    issue(0);
+    // flight while the first tile is processed. (REG: the first four tiles,
+    // into registers.)
+    if constexpr (REG) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) load_tile(k, rb[k]);
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        issue(0);
+    }
     half8 qv[RC ? 1 : KB];
     half8 qb[RC ? 4 : 1][2];   // RC: B operands q[head][d] * scale per 32-row block of d and half
     const int grp = RC ? n_q / ra.n_kv : 32;
@@ -1227,13 +1306,96 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         lds_barrier();   // before the tile region is reused
     }
     const int nt = tiles_before(cend);
+    if constexpr (!REG) {
 #pragma unroll
-    for (int j = 1; j < D - 1; ++j) issue(j);   // a static number of loads (see issue)
+        for (int j = 1; j < D - 1; ++j) issue(j);   // a static number of loads (see issue)
+    }
 
     float m_ref = -INFINITY, l_run = 0.0f;
     floatx16 acc[CB];
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[j] = floatx16{};
+
+    // Absorbed queries below GP 128 (FRAME): scores come out of the MFMAs already shifted
+    // into the wave's frame. With codes as 1024 + n (unpack_codes_x16n) the
+    // product sum S of a head is in log2 units; the score MFMAs start from cfr
+    // instead of zero, so element r of a lane ends as S + fr - 4 o(r), where fr
+    // is the head's frame and o(r) = 1 for the token slots the pooling reads 16x
+    // (elements 2, 3, 6, 7, 10, 11, 14, 15): exp2 of it is the weight p = 2^(S +
+    // fr), or p / 16 at those slots, with no subtraction or scaling on the VALU.
+    // The frame is set by the first step's maximum and lowered only when a
+    // weight would leave fp16 (p >= 65520 is converted to infinity, which makes
+    // the step's normaliser infinite): then the step is redone against its own
+    // maximum (a rare path). Weights stay below 2^16 x 16, the frame never rises
+    // above the running maximum, and -fr plays the part of the running max m.
+    float fr = 0.0f;
+    bool fresh = true;   // no step seen yet (wave-uniform)
+    const X16nConst xc = x16n_const();
+    floatx16 cfr_keep;
+    auto set_cfr = [&]() {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cfr_keep[r] = ((r >> 1) & 1) ? fr - 4.0f : fr;
+    };
+    auto cfr = [&]() { return cfr_keep; };
+    set_cfr();
+    // weights of NTL scored tiles (ph[u][i] = elements 2i, 2i + 1 of tile u, in
+    // fp16), the normaliser of exactly those fp16 values (x16 at the 1/16
+    // slots), the frame's rare updates
+    auto weigh = [&](auto ntl_c, auto &sc, const auto &ntok, auto &ph) {
+        constexpr int NTL = decltype(ntl_c)::value;
+#pragma unroll
+        for (int u = 0; u < NTL; ++u)
+            if (ntok[u] < kTile) {   // the chunk's last tile only (uniform)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = (r >> 2) * 8 + hh * 4 + (r & 3);
+                    sc[u][r] = tok < ntok[u] ? sc[u][r] : -INFINITY;
+                }
+            }
+        const half2 one2 = {(_Float16)1.0f, (_Float16)1.0f}, c16 = {(_Float16)16.0f, (_Float16)16.0f};
+        float psum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NTL; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e0 = __builtin_amdgcn_exp2f(sc[u][2 * i]), e1 = __builtin_amdgcn_exp2f(sc[u][2 * i + 1]);
+                ph[u][i] = half2{(_Float16)e0, (_Float16)e1};
+                psum = __builtin_amdgcn_fdot2(ph[u][i], (i & 1) ? c16 : one2, psum, false);
+            }
+        if (__builtin_expect(fresh || __any(!(psum < INFINITY)), 0)) {
+            // the step's maximum of S + fr per head (slot offsets undone)
+            float tm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < NTL; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tm = fmaxf(tm, ((r >> 1) & 1) ? sc[u][r] + 4.0f : sc[u][r]);
+            tm = halves_max(tm);
+            const float fr_new = (fresh || tm > kRescaleSlack) ? fr - tm : fr;
+            const float d = fr_new - fr;
+            if (!fresh) {
+                const float alpha = __builtin_amdgcn_exp2f(d);
+                l_run *= alpha;
+                if (__any(d != 0.0f)) {
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+                }
+            }
+            fr = fr_new;
+            fresh = false;
+            set_cfr();
+            psum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < NTL; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e0 = __builtin_amdgcn_exp2f(sc[u][2 * i] + d);
+                    const float e1 = __builtin_amdgcn_exp2f(sc[u][2 * i + 1] + d);
+                    ph[u][i] = half2{(_Float16)e0, (_Float16)e1};
+                    psum = __builtin_amdgcn_fdot2(ph[u][i], (i & 1) ? c16 : one2, psum, false);
+                }
+        }
+        l_run += psum;
+    };
 
     // transposed-read source row of this lane: nibble d of the result is token
     // row (16 hh + (d & 8) + sigma^-1(d & 7)); see the unpack order
@@ -1243,87 +1405,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     const uint32_t tr_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)trsrc;
     uint8_t *tdst = tile + tile_row(t) * TS + hh * (GP / 4);
 
-    if constexpr (C::PAIR && !RC) {
+    if constexpr (REG) {
         // Two tiles per step: two independent score chains, one softmax update
-        // (max, rescale) for 64 tokens, and pooling from two nibble tiles, which
-        // gives a wave twice the independent work between its waits. Tiles j and
-        // j + 1 sit in slots j % D and (j + 1) % D; this step refills the slots
-        // the previous step emptied, keeping D - 2 tiles in flight beyond it.
-        constexpr int kWaitPair = (((D - 2) * NI) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((D - 2) * NI) >> 4) << 14);
-        auto step = [&](auto ntl_c, int j) {
+        // for 64 tokens, and pooling from two nibble tiles, which gives a wave
+        // twice the independent work between its waits. The registers hold
+        // four tiles: a step takes tiles j, j + 1 from one pair of buffers and
+        // refills that pair with tiles j + 4, j + 5, so two steps of codes are
+        // in flight; the compiler's waits count exactly those loads.
+        auto step = [&](auto ntl_c, int j, auto &x0, auto &x1) {
             constexpr int NTL = decltype(ntl_c)::value;
             uint32_t cur[NTL][KB];
             int ntok[NTL];
 #pragma unroll
             for (int u = 0; u < NTL; ++u) {
-                const int64_t t0 = tile_t0(j + u);
-                const int64_t rem = cend - t0;
+                const int64_t rem = cend - tile_t0(j + u);
                 ntok[u] = rem < kTile ? (int)rem : kTile;
-                const uint8_t *slot = ring + ((j + u) % D) * SLOTB;
-                slot_row<GP, AL>(slot, t, hh, P, AL ? 0 : (int)((uintptr_t)(seq + (size_t)t0 * P) & 15), cur[u]);
+                const auto &x = u == 0 ? x0 : x1;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)   // (v_alignbit: no register pairs)
+                    cur[u][kb] = __builtin_amdgcn_alignbit(x[kb + 1], x[kb], fsh);
 #pragma unroll
                 for (int i = 0; i < KB / 2; ++i)
                     *reinterpret_cast<uint2 *>(tdst + u * 32 * TS + 8 * i) = uint2{cur[u][2 * i], cur[u][2 * i + 1]};
             }
-            // scores, the tiles' chains interleaved
+            if constexpr (NTL == 2) {
+                load_tile(j + 4, x0);
+                load_tile(j + 5, x1);
+            }
+            // scores, the tiles' chains interleaved, each started from the frame
             floatx16 sc[NTL];
 #pragma unroll
-            for (int u = 0; u < NTL; ++u) sc[u] = floatx16{};
+            for (int u = 0; u < NTL; ++u)
+                sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16n(cur[u][0], xc), qv[0], cfr(), 0, 0, 0);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 1; kb < KB; ++kb)
 #pragma unroll
                 for (int u = 0; u < NTL; ++u)
-                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[u][kb]), qv[kb], sc[u], 0, 0, 0);
-            // online softmax over the step's tokens (lane: head t, tokens tok(r))
-            float sv[NTL][16];
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < NTL; ++u) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sv[u][r] = sc[u][r];
-                if (ntok[u] < kTile) {   // the chunk's last tile only (uniform)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int tok = (r >> 2) * 8 + hh * 4 + (r & 3);
-                        sv[u][r] = tok < ntok[u] ? sv[u][r] : -INFINITY;
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[u][r]);
-            }
-            tmax = halves_max(tmax) * kSS;
-            const bool bump = tmax > m_ref + kRescaleSlack;
-            const float m_new = bump ? tmax : m_ref;
-            const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-            const bool rescale = bump && m_ref != -INFINITY;
-            m_ref = m_new;
+                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16n(cur[u][kb], xc), qv[kb], sc[u], 0, 0, 0);
+            // weights of the step's tokens (lane: head t, tokens tok(r))
             half2 ph[NTL][8];
-            float psum = 0.0f;
-            const half2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-            for (int u = 0; u < NTL; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[u][2 * i], kSS, -m_new));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[u][2 * i + 1], kSS, -m_new));
-                    ph[u][i] = half2{(_Float16)e0, (_Float16)e1};
-                    psum = __builtin_amdgcn_fdot2(ph[u][i], one2, psum, false);
-                }
-            l_run = l_run * alpha + psum;
-            if (__any(rescale)) {
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
-            }
+            weigh(ntl_c, sc, ntok, ph);
             // pooling (B operands as in the one-tile loop below)
-            const half2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
             v2i32 zt[NTL][CB];
 #pragma unroll
             for (int u = 0; u < NTL; ++u) tr4_reads<CB>(tr_addr + u * 32 * TS, zt[u]);
 #pragma unroll
             for (int u = 0; u < NTL; ++u) {
-                const half2 q1 = ph[u][1] * s16, q3 = ph[u][3] * s16, q5 = ph[u][5] * s16, q7 = ph[u][7] * s16;
-                const half8 pv0 = {ph[u][0].x, ph[u][0].y, q1.x, q1.y, ph[u][2].x, ph[u][2].y, q3.x, q3.y};
-                const half8 pv1 = {ph[u][4].x, ph[u][4].y, q5.x, q5.y, ph[u][6].x, ph[u][6].y, q7.x, q7.y};
+                const half8 pv0 = {ph[u][0].x, ph[u][0].y, ph[u][1].x, ph[u][1].y, ph[u][2].x, ph[u][2].y, ph[u][3].x, ph[u][3].y};
+                const half8 pv1 = {ph[u][4].x, ph[u][4].y, ph[u][5].x, ph[u][5].y, ph[u][6].x, ph[u][6].y, ph[u][7].x, ph[u][7].y};
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16((uint32_t)zt[u][cb][0]), pv0, acc[cb], 0, 0, 0);
@@ -1331,22 +1460,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
                 }
             }
         };
+        constexpr std::integral_constant<int, 2> two{};
+        constexpr std::integral_constant<int, 1> one{};
+        // tiles with no bounds concerns: all but (possibly) the capacity-end one
+        const int64_t fast_end = seq_cap - kTile < cend ? seq_cap - kTile : cend;
+        const int nf = tiles_before(fast_end);
         int j = 0;
-        for (; j + 1 < nt; j += 2) {
-            // refill the slots of tiles j - 2 and j - 1 (at j = 0: slot D - 1,
-            // the one the prologue left free)
-            const int lo = j + D - 2 > D - 1 ? j + D - 2 : D - 1;
-            for (int k = lo; k <= j + D - 1; ++k)
-                if (k < nt) issue(k);
-            if (j + D <= nt)   // tiles j + 2 .. j + D - 1 may stay in flight
-                __builtin_amdgcn_s_waitcnt(kWaitPair);
-            else
-                __builtin_amdgcn_s_waitcnt(kWaitAll);
-            step(std::integral_constant<int, 2>{}, j);
+        for (; j + 3 < nf; j += 4) {
+            step(two, j, rb[0], rb[1]);
+            step(two, j + 2, rb[2], rb[3]);
         }
-        if (j < nt) {   // an odd last tile
-            __builtin_amdgcn_s_waitcnt(kWaitAll);
-            step(std::integral_constant<int, 1>{}, j);
+        if (j + 1 < nf) {
+            step(two, j, rb[0], rb[1]);
+            if (j + 2 < nf) step(one, j + 2, rb[2], rb[3]);
+        } else if (j < nf) {
+            step(one, j, rb[0], rb[1]);
+        }
+        if (nf < nt) {   // the capacity-end tile (this wave's last): dwords past
+                         // the sequence's last one are clamped to it
+            const uint8_t *tb = sb + (size_t)tile_t0(nt - 1) * P + voff;
+            uint32_t rx[NLD];
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const uint8_t *a = tb + 4 * i;
+                rx[i] = *reinterpret_cast<const uint32_t *>(a < lastdw ? a : lastdw);
+            }
+            step(one, nt - 1, rx, rx);
         }
     } else
     for (int j = 0; j < nt; ++j) {
@@ -1373,7 +1512,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
 
         // ---- scores of the tile's 32 tokens for the 32 heads (units of 2^-24)
         floatx16 sc = floatx16{};
-        if constexpr (!RC) {
+        if constexpr (FRAME) {   // started from the frame (see weigh), accumulated in place
+            sc = cfr();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16n(cur[kb], xc), qv[kb], sc, 0, 0, 0);
+        } else if constexpr (!RC) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(unpack_codes_x16(cur[kb]), qv[kb], sc, 0, 0, 0);
@@ -1454,6 +1598,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
             }
         }
 
+        half8 pv0, pv1;
+        if constexpr (FRAME) {
+            floatx16 sc1[1] = {sc};
+            const int nt1[1] = {ntok};
+            half2 ph[1][8];
+            weigh(std::integral_constant<int, 1>{}, sc1, nt1, ph);
+            pv0 = half8{ph[0][0].x, ph[0][0].y, ph[0][1].x, ph[0][1].y, ph[0][2].x, ph[0][2].y, ph[0][3].x, ph[0][3].y};
+            pv1 = half8{ph[0][4].x, ph[0][4].y, ph[0][5].x, ph[0][5].y, ph[0][6].x, ph[0][6].y, ph[0][7].x, ph[0][7].y};
+        } else {
         // ---- online softmax of this wave (lane: head t, tokens tok(r))
         float sv[16];
 #pragma unroll
@@ -1495,8 +1648,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
         // source rows of the transposed read), so their weights are scaled by 1/16
         const half2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
         const half2 q1 = ph[1] * s16, q3 = ph[3] * s16, q5 = ph[5] * s16, q7 = ph[7] * s16;
-        const half8 pv0 = {ph[0].x, ph[0].y, q1.x, q1.y, ph[2].x, ph[2].y, q3.x, q3.y};
-        const half8 pv1 = {ph[4].x, ph[4].y, q5.x, q5.y, ph[6].x, ph[6].y, q7.x, q7.y};
+        pv0 = half8{ph[0].x, ph[0].y, q1.x, q1.y, ph[2].x, ph[2].y, q3.x, q3.y};
+        pv1 = half8{ph[4].x, ph[4].y, q5.x, q5.y, ph[6].x, ph[6].y, q7.x, q7.y};
+        }
 
         // ---- pooling: acc[cb][coordinate 32 cb + m][head] += z^T p
         v2i32 zt[CB];
@@ -1512,6 +1666,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // zbar = 2^24 sum c_w acc_w / L - 8, summed in wave order
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // prologue loads past the length may be in flight
     lds_barrier();                          // every wave is done with its ring and tile
+    if constexpr (FRAME) m_ref = fresh ? -INFINITY : -fr;
     const float l_w = halves_sum(l_run);
     if (lane < 32) {
         ms[wave][lane] = m_ref;

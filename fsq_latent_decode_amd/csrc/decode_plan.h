@@ -69,7 +69,9 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     const int starget = stream_target(p.GP);
     int64_t sper = (work + starget - 1) / starget;
     sper = (sper + squant - 1) / squant * squant;
-    p.stream = allow_stream && sper >= (int64_t)kStreamMinTiles * squant ? 1 : 0;
+    // (and only for caches of 64 rows or more: below GP 128 its unchecked
+    // register loads may read into the row after a tile)
+    p.stream = allow_stream && sper >= (int64_t)kStreamMinTiles * squant && seq_cap >= 64 ? 1 : 0;
     p.waves = p.stream ? kStreamWaves : split_waves(p.GP, work);
     const int quantum = 32 * p.waves;
     const int target = p.stream ? starget : (p.waves == 8 ? 256 : 512);
