@@ -1080,7 +1080,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // The ring (the only target of direct-to-LDS loads) and the nibble tiles are
     // distinct LDS objects, so the compiler's waits for those loads do not
     // extend to the tile stores.
-    __shared__ __attribute__((aligned(16))) uint8_t ring_lds[C::RINGA];
+    // REG (below GP 128, absorbed queries) uses this space only to combine the
+    // waves, all coordinate blocks at once
+    constexpr bool REGC = C::PAIR && !RC;
+    constexpr int RING_BYTES = REGC ? C::CB * C::CBYTES : C::RINGA;
+    __shared__ __attribute__((aligned(16))) uint8_t ring_lds[RING_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t tile_lds[C::TILE];
     __shared__ __attribute__((aligned(16))) _Float16 wk_lds[RC ? kReconMaxDh * WROW : 8];
     __shared__ float gam_lds[RC == 2 ? kReconMaxDh : 1];
@@ -1188,7 +1192,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     // the dwords around its half of its token's row straight into registers,
     // four tiles ahead (REG below); the ring and its LDS reads serve the wider
     // latents and the key-reconstruction variants.
-    constexpr bool REG = C::PAIR && !RC;
+    constexpr bool REG = REGC;
     // dwords per lane and tile (REG): the KB + 1 aligned dwords around the
     // lane's half (funnel-shifted by its byte offset) for every row alignment
     constexpr int NLD = KB + 1;
@@ -1664,6 +1668,60 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
 
     // ---- combine the waves: M = max m_w, c_w = 2^(m_w - M), L = sum c_w l_w,
     // zbar = 2^24 sum c_w acc_w / L - 8, summed in wave order
+    const int heads = RC ? grp : ((n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32);
+    const size_t pbase = ((size_t)b * n_q + hg * (RC ? grp : 32)) * S + s;   // head-major partial rows
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    if constexpr (REG) {
+        // Every wave's (m, l) and unscaled sums go to LDS (which nothing else
+        // uses here) before one barrier; wave cb % NW then weighs and sums
+        // block cb of all waves.
+        m_ref = fresh ? -INFINITY : -fr;
+        const float l_w = halves_sum(l_run);
+        if (lane < 32) {
+            ms[wave][lane] = m_ref;
+            ls[wave][lane] = l_w;
+        }
+        floatx4 *cbuf = reinterpret_cast<floatx4 *>(ring_lds);   // [block][wave][4][64 lanes]
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                cbuf[((cb * NW + wave) * 4 + e) * 64 + lane] =
+                    floatx4{acc[cb][4 * e], acc[cb][4 * e + 1], acc[cb][4 * e + 2], acc[cb][4 * e + 3]};
+        __builtin_amdgcn_s_waitcnt(kWaitAll);   // the loads of tiles past the chunk
+        lds_barrier();
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ms[w][t]);
+        float L = 0.0f, cw[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = ms[w][t];
+            cw[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+            L += cw[w] * ls[w][t];
+        }
+        const float zscale = kCodeScale / L;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (cb % NW == wave && t < heads) {
+                _Float16 *dst = part_z + (pbase + (size_t)t * S) * GP + cb * 32 + hh * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    floatx4 sum = cbuf[((cb * NW + 0) * 4 + e) * 64 + lane] * cw[0];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w) sum += cbuf[((cb * NW + w) * 4 + e) * 64 + lane] * cw[w];
+                    const half4 v = {(_Float16)fmaf(sum[0], zscale, -8.0f), (_Float16)fmaf(sum[1], zscale, -8.0f),
+                                     (_Float16)fmaf(sum[2], zscale, -8.0f), (_Float16)fmaf(sum[3], zscale, -8.0f)};
+                    *reinterpret_cast<half4 *>(dst + 8 * e) = v;
+                }
+            }
+        }
+        if (wave == 0 && lane < heads) {
+            part_ml[(pbase + (size_t)lane * S) * 2 + 0] = M;
+            part_ml[(pbase + (size_t)lane * S) * 2 + 1] = L;
+        }
+        return;
+    }
     __builtin_amdgcn_s_waitcnt(kWaitAll);   // prologue loads past the length may be in flight
     lds_barrier();                          // every wave is done with its ring and tile
     if constexpr (FRAME) m_ref = fresh ? -INFINITY : -fr;
@@ -1684,10 +1742,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     }
     const float cw = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
     const float zscale = kCodeScale / L;
-    const int heads = RC ? grp : ((n_q - hg * 32) < 32 ? (n_q - hg * 32) : 32);
-    const size_t pbase = ((size_t)b * n_q + hg * (RC ? grp : 32)) * S + s;   // head-major partial rows
     floatx4 *cbuf = reinterpret_cast<floatx4 *>(ring_lds);   // [block][wave][4][64 lanes]
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int p0 = 0; p0 < CB; p0 += C::BPP) {
 #pragma unroll
