@@ -992,18 +992,21 @@ __device__ inline half8 unpack_codes_centered(uint32_t w) {
 
 // Device-side split of the streaming kernel (kDynMaxBatch sequences or fewer):
 // the chunk is chosen from the actual lengths, so that the sum of all
-// sequences' tokens spreads over ncta CTAs in whole rounds of kStreamWaves
-// tiles, at least chunk_min (which bounds a sequence's split count by the
+// sequences' tokens spreads over ncta CTAs in whole rounds of q tokens (the
+// CTA's waves x 32), at least chunk_min (which bounds a sequence's split count by the
 // workspace's). Sequence b then has ceil(T_b / chunk) work items, numbered
 // consecutively over the sequences; CTA i takes item i. Every wave of a CTA
 // computes this the same way: lane b holds T_b (one vector load), a wave sum
 // gives the total, a prefix scan of the item counts locates item i.
-__device__ inline int stream_dyn_chunk(int64_t total, int ncta, int chunk_min) {
-    constexpr int64_t q = 32 * kStreamWaves;
-    // ceil(total / ncta) by an fp64 division: total < 2^37 and ncta <= 2^10, so
-    // the correctly rounded quotient is within 2^-15 of the exact one, whose
-    // fraction is 0 or at least 2^-10: its floor is the integer quotient
-    int64_t c = (int64_t)floor((double)(total + ncta - 1) / (double)ncta);
+__device__ inline int stream_dyn_chunk(int64_t total, int ncta, int nseq, int chunk_min, int64_t q) {
+    // ceil(total / (ncta - nseq)): each sequence rounds its item count up by at
+    // most one, so sum_b ceil(T_b / chunk) <= total / chunk + nseq <= ncta and
+    // every item has a CTA of the one resident set (nseq <= 64 <= ncta / 4).
+    // By an fp64 division: total < 2^37 and n <= 2^10, so the correctly rounded
+    // quotient is within 2^-15 of the exact one, whose fraction is 0 or at
+    // least 2^-10: its floor is the integer quotient
+    const int n = ncta - nseq;
+    int64_t c = (int64_t)floor((double)(total + n - 1) / (double)n);
     c = (c + q - 1) / q * q;
     return (int)(c < chunk_min ? chunk_min : c);
 }
@@ -1047,12 +1050,12 @@ __device__ inline uint32_t wave_scan_u32(uint32_t v) {
     return x;
 }
 // lane's clamped length T_lane (0 past the batch) and the chunk
-__device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int batch, int64_t seq_cap,
+__device__ inline int stream_dyn_lens(const int32_t *__restrict__ seq_lens, int batch, int64_t seq_cap, int64_t q,
                                       int ncta, int chunk_min, int lane, int64_t &t_lane) {
     int64_t T = lane < batch ? (int64_t)seq_lens[lane] : 0;
     T = T < 0 ? 0 : (T > seq_cap ? seq_cap : T);
     t_lane = T;
-    return stream_dyn_chunk(wave_sum64(T), ncta, chunk_min);
+    return stream_dyn_chunk(wave_sum64(T), ncta, batch, chunk_min, q);
 }
 
 template <int GP, int NW, int D, bool AL, int RC>
@@ -1120,14 +1123,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RC ? 1 
     if (dyn_batch == 1) {   // one sequence: item i is chunk i of it
         int64_t T0 = seq_lens[0];
         T0 = T0 < 0 ? 0 : (T0 > seq_cap ? seq_cap : T0);
-        chunk = stream_dyn_chunk(T0, ncta, chunk_arg);
+        chunk = stream_dyn_chunk(T0, ncta, 1, chunk_arg, 32 * NW);
         b = 0;
         s = blockIdx.x;
         if ((int64_t)s * chunk >= T0) return;   // no work left (uniform)
         T_dyn = T0;
     } else if (dyn_batch > 0) {
         int64_t t_lane;
-        chunk = stream_dyn_lens(seq_lens, dyn_batch, seq_cap, ncta, chunk_arg, lane, t_lane);
+        chunk = stream_dyn_lens(seq_lens, dyn_batch, seq_cap, 32 * NW, ncta, chunk_arg, lane, t_lane);
         const int n = (int)(((uint32_t)t_lane + (uint32_t)chunk - 1u) / (uint32_t)chunk);   // this lane's sequence's items (T < 2^31)
         const int incl = (int)wave_scan_u32((uint32_t)n);
         const int item = blockIdx.x;
@@ -1813,6 +1816,7 @@ struct MergeGeom {
     int tpp_log2;   // level-two threads per position: 1 << tpp_log2
     int ZS;         // zpart row stride (floats)
     int g_mul;      // ceil(2^20 / (n_q / n_kv)): kv head of query head h < 64
+    int dyn_q;      // device split: the streaming CTA's round (waves x 32 tokens)
 };
 constexpr int kMergeMaxS = 1024;
 
@@ -1871,7 +1875,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     if (dyn_batch > 0) {
         const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
         const int64_t tl = (tid & 63) >= dyn_batch || tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
-        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, dyn_batch, chunk_arg, geo.dyn_q);
     }
     // T < 2^31 and chunk < 2^30: the split count in 32-bit arithmetic
     const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
@@ -2081,7 +2085,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     if (dyn_batch > 0) {
         const int64_t tb = T_raw < 0 ? 0 : (T_raw > seq_cap ? seq_cap : (int64_t)T_raw);
         const int64_t tl = lane >= dyn_batch || tl_raw < 0 ? 0 : (tl_raw > seq_cap ? seq_cap : (int64_t)tl_raw);
-        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, chunk_arg);
+        chunk = stream_dyn_chunk(dyn_batch == 1 ? tb : wave_sum64(tl), ncta, dyn_batch, chunk_arg, geo.dyn_q);
     }
     const uint32_t T = T_raw < 0 ? 0u : (T_raw > seq_cap ? (uint32_t)seq_cap : (uint32_t)T_raw);
     const int ns = (int)((T + (uint32_t)chunk - 1u) / (uint32_t)chunk);
@@ -2176,6 +2180,7 @@ static hipError_t launch_merge(const _Float16 *pz, const float *pml, const uint1
     geo.ZS = GP + (geo.tpp_log2 == 5 ? 4 : 64 >> geo.tpp_log2);
     const int grp = n_q / n_kv;
     geo.g_mul = ((1 << 20) + grp - 1) / grp;
+    geo.dyn_q = 32 * stream_waves(GP);
     // the one-barrier merge: one coordinate group per 64-lane wave (widths up to
     // 128) or per 32-lane half (up to 256), at most 4 splits per lane; more
     // splits (long single sequences) take the two-level kernel
@@ -2255,7 +2260,7 @@ static hipError_t launch_stream_d(const DecodePlan &pl, const _Float16 *qt, cons
                                   const int32_t *seq_lens, _Float16 *pz, float *pml, int64_t seq_cap,
                                   int G, int n_q, int batch, hipStream_t st, hipEvent_t ev0,
                                   hipEvent_t ev1) {
-    constexpr int NW = kStreamWaves;
+    constexpr int NW = GP < 128 ? 8 : 4;   // stream_waves(GP)
     // device-side split: ncta + batch CTAs cover every work item (the per-sequence
     // rounding up adds at most one item per sequence)
     dim3 grid(pl.dyn ? pl.ncta + batch : pl.S, pl.dyn ? 1 : batch, pl.nqp / 32);
@@ -2312,7 +2317,7 @@ static hipError_t launch_split(const DecodePlan &pl, const _Float16 *qt, const u
                                                                  batch, st, ev0, ev1);
     }
     if (pl.stream) {
-        if (pl.waves != kStreamWaves) return hipErrorInvalidValue;
+        if (pl.waves != stream_waves(GP)) return hipErrorInvalidValue;
         constexpr int D = GP >= 128 ? 3 : 4;   // stream_depth(GP)
         if (stream_depth(GP) != D) return hipErrorInvalidValue;
         return launch_stream_d<GP, D>(pl, qt, codes, seq_lens, pz, pml, seq_cap, G, n_q, batch, st,

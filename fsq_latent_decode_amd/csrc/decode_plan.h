@@ -22,12 +22,16 @@ inline int split_waves(int GP, int64_t work) {
     return (GP >= 128 || (GP >= 64 && work >= (int64_t)2 * 256 * 256)) ? 8 : 4;
 }
 
-// Streaming split (long chunks): 4-wave CTAs, each wave keeping stream_depth - 1
-// tiles of codes in flight. Registers and LDS allow two CTAs per CU when
-// GP >= 128 and three below, so 512 or 768 CTAs (one resident set) are aimed
-// for. It is chosen when every wave gets at least kStreamMinTiles tiles of 32
-// tokens.
+// Streaming split (long chunks). GP >= 128: 4-wave CTAs, each wave keeping
+// stream_depth - 1 tiles of codes in flight through an LDS ring; registers and
+// LDS allow two CTAs per CU, so 512 CTAs (one resident set) are aimed for.
+// Below GP 128: 8-wave CTAs whose waves keep four tiles in registers, one CTA
+// per CU (two waves per SIMD), 256 CTAs: half the partial rows of 4-wave CTAs
+// at the same occupancy. It is chosen when every wave gets at least
+// kStreamMinTiles tiles of 32 tokens. (The key-reconstruction variants use
+// 4-wave CTAs at every width: kStreamWaves.)
 constexpr int kStreamWaves = 4;
+inline int stream_waves(int GP) { return GP < 128 ? 8 : 4; }
 constexpr int kStreamMinTiles = 4;
 // Streaming calls of up to kDynMaxBatch sequences split on the device from the
 // actual lengths (one lane per sequence there); the chunk is then at least
@@ -36,12 +40,12 @@ constexpr int kStreamMinTiles = 4;
 constexpr int kDynMaxBatch = 64;
 constexpr int kDynMaxSplits = 1024;
 inline int stream_depth(int GP) { return GP >= 128 ? 3 : 4; }
-inline int stream_target(int GP) { return GP >= 128 ? 512 : 768; }
-// Work items of the device-side split: 512 at every width. Below GP 128 this is
-// two of the three resident CTAs per CU: longer chunks and a third fewer
-// partial rows to merge (measured on the MI355X: a 1M-token G=84 layer 38.8 vs
-// 41.5 us with 768).
-constexpr int kDynCtas = 512;
+inline int stream_target(int GP) { return GP >= 128 ? 512 : 256; }
+// Work items of the device-side split: one resident set of CTAs (512 of 4
+// waves at GP >= 128, 256 of 8 waves below; measured on the MI355X with 4-wave
+// CTAs: a 1M-token G=84 layer 38.8 us with 512 items vs 41.5 with 768).
+inline int dyn_ctas(int GP) { return GP >= 128 ? 512 : 256; }
+static_assert(kDynMaxBatch * 4 <= 256, "the device split spreads over ncta - batch CTAs");
 
 struct DecodePlan {
     int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
@@ -65,14 +69,14 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     p.GP = (G + 31) / 32 * 32;
     p.nqp = (n_q + 31) / 32 * 32;
     const int64_t work = int64_t(batch) * seq_cap;
-    const int squant = 32 * kStreamWaves;
+    const int squant = 32 * stream_waves(p.GP);
     const int starget = stream_target(p.GP);
     int64_t sper = (work + starget - 1) / starget;
     sper = (sper + squant - 1) / squant * squant;
     // (and only for caches of 64 rows or more: below GP 128 its unchecked
     // register loads may read into the row after a tile)
     p.stream = allow_stream && sper >= (int64_t)kStreamMinTiles * squant && seq_cap >= 64 ? 1 : 0;
-    p.waves = p.stream ? kStreamWaves : split_waves(p.GP, work);
+    p.waves = p.stream ? stream_waves(p.GP) : split_waves(p.GP, work);
     const int quantum = 32 * p.waves;
     const int target = p.stream ? starget : (p.waves == 8 ? 256 : 512);
     int64_t per = (work + target - 1) / target;
@@ -80,7 +84,7 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     per = (per + quantum - 1) / quantum * quantum;
     if (p.stream && batch <= kDynMaxBatch) {
         p.dyn = 1;
-        p.ncta = kDynCtas;
+        p.ncta = dyn_ctas(p.GP);
         int64_t cmin = (seq_cap + kDynMaxSplits - 1) / kDynMaxSplits;
         if (cmin < (int64_t)kStreamMinTiles * squant) cmin = (int64_t)kStreamMinTiles * squant;
         per = (cmin + squant - 1) / squant * squant;
@@ -88,6 +92,9 @@ inline DecodePlan make_decode_plan(int batch, int n_q, int G, int64_t seq_cap, b
     if (per > (int64_t)1 << 30) per = (int64_t)1 << 30;
     p.chunk = (int)per;
     p.S = (int)((seq_cap + p.chunk - 1) / p.chunk);
+    // device split: the chunk is at least ceil(sum of lengths / ncta), so no
+    // sequence has more than ncta work items
+    if (p.dyn && p.S > p.ncta) p.S = p.ncta;
     const int S1 = p.S > 0 ? p.S : 1;
     p.off_qt = 0;
     // q~ in fp16, two terms (8-bit codes use the second: the rounding residual)

@@ -3,6 +3,7 @@
 // tests/test_host_sanitized.py with g++ -fsanitize=address,undefined (every
 // report fatal) and run there; any overflow, out-of-bounds access or failed
 // expectation ends the program with a nonzero status.
+#include <algorithm>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -34,10 +35,14 @@ static void check_plan(const DecodePlan &p, int32_t batch, int32_t n_q, int32_t 
     EXPECT(p.waves == 4 || p.waves == 8);
     EXPECT(p.chunk > 0 && p.chunk % (32 * p.waves) == 0);
     if (cap == 0) EXPECT(p.S == 0);
-    else EXPECT((int64_t)p.S * p.chunk >= cap && (int64_t)(p.S - 1) * p.chunk < cap);
+    else if (!p.dyn) EXPECT((int64_t)p.S * p.chunk >= cap && (int64_t)(p.S - 1) * p.chunk < cap);
+    // device split: S bounds the work items of any sequence, ceil(T / chunk)
+    // with chunk >= max(chunk_min, sum of lengths / ncta): at most ncta
+    else EXPECT(p.S == std::min<int64_t>((cap + p.chunk - 1) / p.chunk, p.ncta));
     EXPECT(!p.stream || stream_ok);
-    EXPECT(!p.dyn || (p.stream && batch <= fsq::kDynMaxBatch && p.ncta == fsq::kDynCtas));
-    if (p.dyn) EXPECT(p.chunk >= fsq::kStreamMinTiles * 32 * fsq::kStreamWaves && (int64_t)p.chunk * fsq::kDynMaxSplits >= cap);
+    EXPECT(!p.stream || p.waves == fsq::stream_waves(p.GP));
+    EXPECT(!p.dyn || (p.stream && batch <= fsq::kDynMaxBatch && p.ncta == fsq::dyn_ctas(p.GP)));
+    if (p.dyn) EXPECT(p.chunk >= fsq::kStreamMinTiles * 32 * p.waves && (int64_t)p.chunk * fsq::kDynMaxSplits >= cap);
     // workspace: q~ rows, then fp16 zbar partials, then (m, l) pairs, each
     // region 256-byte aligned and large enough for every split of the plan
     const size_t S1 = p.S > 0 ? (size_t)p.S : 1;
@@ -104,13 +109,13 @@ static void decode_cases() {
     EXPECT(decode(2, 32, 8, 128, 84, ((int64_t)1 << 40) / 2 + 1, big) == FSQ_ERR_UNSUPPORTED);
     EXPECT(decode(INT32_MAX, FSQ_MAX_NQ, 1, FSQ_MAX_DH, FSQ_MAX_G, INT64_MAX, SIZE_MAX) == FSQ_ERR_UNSUPPORTED);
     // the allocation-free entry point's capacity check: the per-layer
-    // workloads fit its scratch area, the layer-batched calls do not
+    // workloads fit its scratch area, the layer-batched G=256 call does not
     size_t ws_need = 0;
     EXPECT(fsq::validate_decode_args(P, P, P, P, P, 16, 16, 8, 128, 256, 65536, 16, nullptr, &ws_need) == FSQ_OK);
     EXPECT(ws_need <= FSQ_NOALLOC_SCRATCH_BYTES);
     EXPECT(fsq::validate_decode_args(P, P, P, P, P, 1, 32, 8, 128, 84, 1 << 20, 16, nullptr, &ws_need) == FSQ_OK);
     EXPECT(ws_need <= FSQ_NOALLOC_SCRATCH_BYTES);
-    EXPECT(fsq::validate_decode_args(P, P, P, P, P, 36, 32, 8, 128, 84, 131072, 16, nullptr, &ws_need) == FSQ_OK);
+    EXPECT(fsq::validate_decode_args(P, P, P, P, P, 36, 32, 8, 128, 256, 32768, 16, nullptr, &ws_need) == FSQ_OK);
     EXPECT(ws_need > FSQ_NOALLOC_SCRATCH_BYTES);
     // the step's extra arguments
     EXPECT(fsq::validate_step_append(P, P, 1, 4096, 32, 8, 128, 84, 10) == FSQ_OK);

@@ -211,15 +211,20 @@ def test_decode_plan_host_logic():
     for args in [(1, 32, 256, 1), (1, 32, 84, 1 << 20), (16, 16, 256, 65536), (3, 12, 37, 5000),
                  (65, 16, 256, 65536)]:
         p = fsq.decode_plan(*args)
-        assert p["splits"] * p["chunk"] >= args[3] > (p["splits"] - 1) * p["chunk"]
+        if p["device_split"]:   # the chunk is also >= sum of lengths / CTAs: at most that many items
+            ncta = 256 if (args[2] + 31) // 32 * 32 < 128 else 512
+            assert p["splits"] == min(-(-args[3] // p["chunk"]), ncta)
+        else:
+            assert p["splits"] * p["chunk"] >= args[3] > (p["splits"] - 1) * p["chunk"]
         assert p["splits"] <= 1024 and p["chunk"] % 128 == 0
     # streaming calls of up to 64 sequences split on the device from the actual
-    # lengths: the plan then gives the smallest chunk (4 rounds of 4 waves x 32
-    # tokens, and at least seq_cap / 1024) and the largest split count
+    # lengths: the plan then gives the smallest chunk (4 rounds of the CTA's
+    # waves x 32 tokens: 4 waves at width 256, 8 below 128; and at least
+    # seq_cap / 1024) and the largest split count (at most one per CTA)
     p = fsq.decode_plan(16, 16, 256, 65536)
     assert p["device_split"] and p["chunk"] == 512 and p["splits"] == 128
     p = fsq.decode_plan(1, 32, 84, 1 << 20)
-    assert p["device_split"] and p["chunk"] == 1024 and p["splits"] == 1024
+    assert p["device_split"] and p["chunk"] == 1024 and p["splits"] == 256
     assert not fsq.decode_plan(65, 16, 256, 65536)["device_split"]
     assert fsq.decode_plan(65, 16, 256, 65536)["kernel"] == "decode_stream_kernel"
     assert not fsq.decode_plan(1, 32, 256, 32768)["device_split"]

@@ -70,10 +70,10 @@ def test_noalloc_matches_workspace_call_twice_then_smaller(fsq):
 
 
 def test_noalloc_rejects_sizes_beyond_the_scratch_area(fsq):
-    B, n_q, n_kv, d_h, G, cap = 36, 32, 8, 128, 84, 131072
+    B, n_q, n_kv, d_h, G, cap = 36, 32, 8, 128, 256, 32768   # all 36 G=256 layers in one call
     assert fsq.decode_workspace_bytes(B, n_q, G, cap) > fsq.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((B, n_q, d_h), dtype=torch.bfloat16, device="cuda")
-    codes = torch.zeros((B, cap, 42), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((B, cap, (G + 1) // 2), dtype=torch.uint8, device="cuda")
     W = torch.zeros((2 * n_kv * d_h, G), dtype=torch.bfloat16, device="cuda")
     lens = torch.full((B,), cap, dtype=torch.int32, device="cuda")
     out = torch.full((B, n_q, d_h), 3.0, dtype=torch.bfloat16, device="cuda")
