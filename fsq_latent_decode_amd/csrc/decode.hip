@@ -999,13 +999,16 @@ __device__ inline half8 unpack_codes_centered(uint32_t w) {
 // computes this the same way: lane b holds T_b (one vector load), a wave sum
 // gives the total, a prefix scan of the item counts locates item i.
 __device__ inline int stream_dyn_chunk(int64_t total, int ncta, int nseq, int chunk_min, int64_t q) {
-    // ceil(total / (ncta - nseq)): each sequence rounds its item count up by at
-    // most one, so sum_b ceil(T_b / chunk) <= total / chunk + nseq <= ncta and
-    // every item has a CTA of the one resident set (nseq <= 64 <= ncta / 4).
+    // chunk >= total / n with n = ncta - nseq + 1: sequence b has
+    // ceil(T_b / chunk) <= (T_b + chunk - 1) / chunk items, so all of them
+    // number at most total / chunk + nseq - nseq / chunk < n + nseq = ncta + 1,
+    // i.e. at most ncta, and every item has a CTA of the one resident set
+    // (nseq <= 64 <= ncta / 4). One sequence gets exactly ncta items when its
+    // length is a multiple of ncta rounds.
     // By an fp64 division: total < 2^37 and n <= 2^10, so the correctly rounded
     // quotient is within 2^-15 of the exact one, whose fraction is 0 or at
     // least 2^-10: its floor is the integer quotient
-    const int n = ncta - nseq;
+    const int n = ncta - nseq + 1;
     int64_t c = (int64_t)floor((double)(total + n - 1) / (double)n);
     c = (c + q - 1) / q * q;
     return (int)(c < chunk_min ? chunk_min : c);

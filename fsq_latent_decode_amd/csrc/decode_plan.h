@@ -45,7 +45,7 @@ inline int stream_target(int GP) { return GP >= 128 ? 512 : 256; }
 // waves at GP >= 128, 256 of 8 waves below; measured on the MI355X with 4-wave
 // CTAs: a 1M-token G=84 layer 38.8 us with 512 items vs 41.5 with 768).
 inline int dyn_ctas(int GP) { return GP >= 128 ? 512 : 256; }
-static_assert(kDynMaxBatch * 4 <= 256, "the device split spreads over ncta - batch CTAs");
+static_assert(kDynMaxBatch * 4 <= 256, "the device split spreads over ncta - batch + 1 CTAs");
 
 struct DecodePlan {
     int GP = 0;       // G padded to a multiple of 32 (MFMA blocks)
