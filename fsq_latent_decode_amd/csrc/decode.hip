@@ -108,16 +108,16 @@ __device__ inline half8 unpack_codes_x16(uint32_t w) {
 // 1024 sum_k q~_k to every score of a head, a constant that cancels in the
 // softmax and in the merge of splits; in exchange the product is in log2 units
 // already (no 2^24 scale before the exponential).
-// v_and_or_b32 takes no literal operands on this target, so the three
-// constants live in VGPRs (kept there across the tile loop); without the asm
-// the compiler emits a separate AND and OR per operand dword.
-// (an instruction may read one scalar register: the masks are in scalar
-// registers, the exponent bits in a vector register)
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-    return r;
-}
+// v_and_or_b32 takes no literal operands on this target: with the three
+// constants as literals the compiler emits a separate AND and OR per operand
+// dword. Made opaque (x16n_const) they stay in registers (the masks in scalar
+// registers, the exponent bits in a vector register: an instruction may read
+// one scalar register), and the compiler selects one v_and_or_b32 for the C
+// expression. It is written in C, not inline asm, on purpose: an MFMA that
+// reads a VGPR written by an ordinary VALU instruction needs two wait states
+// after it, and the compiler inserts them only for instructions it can see
+// (behind inline asm the MFMA could read the operand's old value).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 struct X16nConst {
     uint32_t lo, hi, e;
 };

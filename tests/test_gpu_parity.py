@@ -268,6 +268,8 @@ def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     (2, 32, 8, 128, 256, 131072, [3000, 1]),
     (2, 32, 8, 128, 256, 131072, [20000, 4097]),
     (4, 32, 8, 128, 84, 131072, [0, 5000, 700, 12345]),
+    (4, 32, 8, 128, 64, 131072, [0, 5000, 700, 12345]),   # whole 1024-token items at widths 64, 32
+    (4, 32, 8, 128, 32, 131072, [0, 5000, 700, 12345]),
     (4, 32, 8, 128, 84, 131073, [65537, 1, 31, 33]),
     (4, 16, 8, 128, 64, 131072, [1000, 65536, 0, 2]),
     (4, 8, 1, 64, 37, 131072, [3001, 129, 1, 64]),
