@@ -4,10 +4,15 @@
 // or 2 / 8 bits for L = 4 / 256 levels (backup frame "the grid size is an
 // allocation choice").
 //
-// Two kernels, chosen by the number of tokens:
-//   append_mfma_kernel  n >= 32: one CTA per 32 tokens, bf16 MFMA 32x32x16 with
-//                       fp32 accumulation; the 4 waves split the C dimension and
-//                       are summed in a fixed order; FSQ + packing in the epilogue.
+// Three kernels, chosen by the number of tokens and the width:
+//   append_stage_kernel n >= 32, GP <= 128: one CTA of 8 waves per 32 tokens,
+//                       bf16 MFMA 32x32x16 with fp32 accumulation over
+//                       CTA-wide k-batches staged in registers several batches
+//                       ahead; the 8 waves' sums added in a fixed order; FSQ +
+//                       packing in the epilogue.
+//   append_mfma_kernel  n >= 32, GP > 128: one CTA of 4 waves per 32 tokens,
+//                       the waves split the C dimension, tiles staged by
+//                       direct-to-LDS loads; the same epilogue.
 //   append_gemv_kernel  n < 32 (a decode step appends one token per sequence):
 //                       one CTA per output byte (a pair of coordinates) and up to
 //                       8 tokens, 16-byte vector loads of E and x, tree reduction.
@@ -178,11 +183,195 @@ __global__ __launch_bounds__(kAppendWaves * 64) __attribute__((amdgpu_waves_per_
     }
 }
 
+// Prefill path for GP <= 128. A CTA of 8 waves computes u = E x for 32 tokens
+// over k-batches of 256: the batch's tile is the 32 x rows and the GP E rows,
+// 512 bytes each (x rows clamped to the last token, E rows to row G - 1: their
+// outputs are never used). Every load instruction moves two whole 512-byte row
+// segments (16 bytes per lane) into registers; a wave's loads run D batches
+// ahead of their use, so a CU keeps D tiles of loads in flight in its register
+// file instead of the few that fit LDS beside the tiles being multiplied. The
+// x rows are loaded non-temporally (read once).
+// When a batch's registers arrive they are written to one of two LDS tiles
+// (16-byte chunk c of row rho at c ^ (rho & 15): the 16 lanes of one pass of a
+// 16-byte LDS access touch 16 distinct 16-byte bank groups, for the row-wise
+// writes and the column-wise operand reads alike), one barrier hands the tile to
+// the CTA, and wave w runs the batch's k-steps 2w and 2w + 1 for all output
+// blocks, reading its MFMA operands with ds_read_b128 (lane = row; k-step s
+// takes chunks 2s and 2s + 1). k past C (the last batch when C % 256 != 0, and
+// the batches that round the count up to a multiple of D) is zeroed in the
+// tile. After the last batch each wave stores its sums to LDS and every output
+// coordinate is the sum over waves 0..7 in that order.
+constexpr int kStageWaves = 8;
+
+// Workgroup barrier for an LDS hand-off: waits for this wave's LDS operations
+// only (__syncthreads would also wait for the staged global loads in flight).
+__device__ __attribute__((always_inline)) inline void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int GP>
+struct StageCfg {
+    static constexpr int KPB = 256;                          // k per batch
+    static constexpr int RL = 2 * KPB;                       // bytes per tile row
+    static constexpr int ROWS = 32 + GP;                     // x rows, then E rows
+    static constexpr int TILE = ROWS * RL;                   // bytes per LDS tile
+    static constexpr int LPW = ROWS / (2 * kStageWaves);     // load instructions per wave and batch
+    static constexpr int D = GP <= 96 ? 4 : 2;               // batches in flight per wave
+    static constexpr int CB = GP / 32;                       // 32-wide output blocks
+    static_assert(ROWS % (2 * kStageWaves) == 0, "two rows per load instruction");
+    static_assert(2 * TILE <= 160 * 1024, "two tiles fit LDS");
+    static constexpr int PS = GP + 8;                        // row stride of the waves' sums (floats)
+    static_assert(kStageWaves * 32 * PS * 4 <= 2 * TILE, "the waves' sums fit the tiles");
+    static_assert(KPB / 16 == 2 * kStageWaves, "two k-steps per wave and batch");
+};
+
+template <int GP>
+__global__ __launch_bounds__(kStageWaves * 64) void append_stage_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ E, uint8_t *__restrict__ codes,
+    int64_t n, int C, int G, FsqQuant fq, int bits) {
+    using S = StageCfg<GP>;
+    constexpr int KPB = S::KPB, RL = S::RL, TILE = S::TILE, LPW = S::LPW, D = S::D, CB = S::CB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TILE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tile0 = (int64_t)blockIdx.x * 32;
+    const int rows = (n - tile0) < 32 ? (int)(n - tile0) : 32;
+    const int r = lane & 31, hh = lane >> 5;
+
+    // Load instruction t of this wave moves tile rows 2 (wave + 8 t) + hh,
+    // 16-byte chunk `r` of their batch segment. (2 * 8 t) & 15 == 0, so the
+    // swizzle of a lane's rows is the same for every t.
+    const uint16_t *src[LPW];
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+        const int row = 2 * (wave + kStageWaves * t) + hh;
+        src[t] = row < 32 ? x + (tile0 + (row < rows ? row : rows - 1)) * (int64_t)C + 8 * r
+                          : E + (int64_t)(row - 32 < G ? row - 32 : G - 1) * C + 8 * r;
+    }
+    const int wrow0 = 2 * wave + hh;
+    const int woff = wrow0 * RL + 16 * (r ^ (wrow0 & 15));   // + t * 2 * kStageWaves * RL
+    // operand reads: row r of the x block / of E block cb, chunk 4 wave + 2 s + hh
+    const int sw = r & 15;
+
+    floatx16 acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[cb] = floatx16{};
+
+    const int nb = (C + KPB - 1) / KPB;
+    const int nbp = (nb + D - 1) / D * D;
+    // CTA b takes the batches in the order b mod nb, b + 1 mod nb, ...: at any
+    // moment the CTAs read different columns of x and E, which spreads their
+    // requests over the memory channels (batches past nb are the all-zero
+    // padding and keep their index)
+    const int rot = (int)(blockIdx.x % (unsigned)nb);
+    auto batch_k = [&](int jb) { return (jb < nb ? (jb + rot < nb ? jb + rot : jb + rot - nb) : jb) * KPB; };
+    u32x4 st[D][LPW];
+    auto load = [&](u32x4(&v)[LPW], int jb) {
+        // lanes whose chunk lies past C read their row's first chunk (zeroed later)
+        const int kb = batch_k(jb);
+        const int ko = kb + 8 * r < C ? kb : -8 * r;
+#pragma unroll
+        for (int t = 0; t < LPW; ++t) {
+            if (t < 32 / (2 * kStageWaves)) {   // x rows: read once, kept out of the caches' reuse
+                v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[t] + ko));
+            } else {
+                v[t] = *reinterpret_cast<const u32x4 *>(src[t] + ko);
+            }
+        }
+    };
+    auto stage = [&](const u32x4(&v)[LPW], int jb, uint8_t *tile) {
+        const int kb = batch_k(jb);
+        if (kb + KPB <= C) {
+#pragma unroll
+            for (int t = 0; t < LPW; ++t)
+                *reinterpret_cast<u32x4 *>(tile + woff + t * 2 * kStageWaves * RL) = v[t];
+        } else {
+            const bool kin = kb + 8 * r < C;
+#pragma unroll
+            for (int t = 0; t < LPW; ++t)
+                *reinterpret_cast<u32x4 *>(tile + woff + t * 2 * kStageWaves * RL) = kin ? v[t] : u32x4{};
+        }
+    };
+    auto compute = [&](const uint8_t *tile) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ch = 16 * ((4 * wave + 2 * s + hh) ^ sw);
+            const u32x4 av = *reinterpret_cast<const u32x4 *>(tile + r * RL + ch);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const u32x4 ev = *reinterpret_cast<const u32x4 *>(tile + (32 + 32 * cb + r) * RL + ch);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                  __builtin_bit_cast(bf16x8, ev), acc[cb], 0,
+                                                                  0, 0);
+            }
+        }
+    };
+    // Stage s of the registers holds batch j0 + s; the tile of batch jb is
+    // jb & 1 (D is even and j0 a multiple of D). Writing tile jb & 1 is safe
+    // once every wave has passed the barrier of batch jb - 1, which each wave
+    // reaches after its reads of batch jb - 2.
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(st[s], s);
+    int j0 = 0;
+    for (; j0 < nbp - D; j0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            uint8_t *tile = lds + (s & 1) * TILE;
+            stage(st[s], j0 + s, tile);
+            stage_barrier();
+            compute(tile);
+            load(st[s], j0 + s + D);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        uint8_t *tile = lds + (s & 1) * TILE;
+        stage(st[s], j0 + s, tile);
+        stage_barrier();
+        compute(tile);
+    }
+    stage_barrier();   // every wave is done with the tiles before they hold the sums
+    // [wave][token][PS]: the two lane halves (tokens 4 apart) on opposite bank halves
+    constexpr int PS = S::PS;
+    float *P = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tok = (i >> 2) * 8 + hh * 4 + (i & 3);
+            P[(wave * 32 + tok) * PS + cb * 32 + r] = acc[cb][i];
+        }
+    stage_barrier();
+    // FSQ + pack: one thread per output byte (8 / bits codes, little-endian)
+    const int cpb = 8 / bits;
+    const int Pb = bytes_per_token_b(G, bits);
+    uint8_t *dst = codes + (size_t)tile0 * Pb;
+    for (int idx = threadIdx.x; idx < rows * Pb; idx += kStageWaves * 64) {
+        const int tok = idx / Pb, j = idx - tok * Pb;
+        uint32_t byte = 0;
+        for (int c = 0; c < cpb; ++c) {
+            const int k = cpb * j + c;
+            if (k < G) {
+                float u = P[tok * PS + k];
+#pragma unroll
+                for (int w = 1; w < kStageWaves; ++w) u += P[(w * 32 + tok) * PS + k];
+                byte |= fsq_code(u, fq) << (bits * c);
+            }
+        }
+        dst[idx] = (uint8_t)byte;
+    }
+}
+
 template <int GP>
 static hipError_t launch_append_mfma(const uint16_t *x, const uint16_t *E, uint8_t *codes,
                                      int64_t n, int C, int G, const FsqQuant &fq, int bits,
                                      hipStream_t st) {
     const int64_t tiles = (n + 31) / 32;
+    if constexpr (GP <= 128) {
+        append_stage_kernel<GP><<<dim3((unsigned)tiles), kStageWaves * 64, 0, st>>>(x, E, codes, n, C, G,
+                                                                                   fq, bits);
+        return hipGetLastError();
+    }
     append_mfma_kernel<GP><<<dim3((unsigned)tiles), kAppendWaves * 64, 0, st>>>(x, E, codes, n, C, G,
                                                                                fq, bits);
     return hipGetLastError();

@@ -85,8 +85,8 @@ def tie_tol(x, E, levels=16):
     """Per-code bound on |u~_fp32 - u~_exact| for the kernels' evaluation of Eq. 2.
 
     u = E x: the bf16 products are exact in fp32, and along any path of the
-    kernels' sums (MFMA K-blocks of 16 accumulated in order, then at most two
-    cross-wave levels; or, for a few tokens, C/64 terms per lane and six
+    kernels' sums (MFMA K-blocks of 16 accumulated in order, then at most seven
+    cross-wave additions; or, for a few tokens, C/64 terms per lane and six
     cross-lane levels) there are at most d = C/16 + 16 rounded fp32 additions,
     so |du| <= gamma_d sum_i |x_i E_i| with gamma_d = d u / (1 - d u) (the
     standard bound for a floating-point dot product, any summation order of
@@ -156,6 +156,10 @@ def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0, levels=16):
     (1, 1024, 64), (5, 512, 83), (17, 256, 7), (31, 4096, 84),     # vector path
     (32, 1024, 64), (33, 1024, 64), (100, 520, 84), (1024, 1024, 64),  # MFMA path, ragged tails
     (257, 2048, 256), (64, 8, 3), (96, 24, 1),
+    # register-staged kernel: two batches in flight (GP = 128), all-zero batches
+    # that round the batch count up to a multiple of four (C = 1288: 6 -> 8), a
+    # k tail inside a batch, many batches at the smallest width
+    (70, 1288, 128), (45, 4096, 120), (40, 1288, 96), (300, 4096, 20),
 ])
 def test_append_parity(fsq, n, C, G):
     g = synth.rng(100, n, C + G)
