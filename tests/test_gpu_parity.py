@@ -160,6 +160,8 @@ def run_append(fsq, x_bits, E_bits, dest_rows=None, row0=0, levels=16):
     # that round the batch count up to a multiple of four (C = 1288: 6 -> 8), a
     # k tail inside a batch, many batches at the smallest width
     (70, 1288, 128), (45, 4096, 120), (40, 1288, 96), (300, 4096, 20),
+    # widths above 128: 128-wide k-batches, sums reduced in passes of 128 codes
+    (45, 136, 161), (64, 8, 200), (96, 4096, 224), (300, 2056, 256),
 ])
 def test_append_parity(fsq, n, C, G):
     g = synth.rng(100, n, C + G)
@@ -174,7 +176,7 @@ def test_append_parity(fsq, n, C, G):
 @pytest.mark.parametrize("levels", [4, 256])
 @pytest.mark.parametrize("n,C,G", [
     (1, 1024, 64), (5, 512, 83), (31, 4096, 84), (32, 1024, 64), (100, 520, 84), (257, 2048, 256),
-    (64, 8, 3), (40, 256, 42), (33, 512, 168),
+    (64, 8, 3), (40, 256, 42), (33, 512, 168), (70, 1288, 250), (96, 4096, 168),
 ])
 def test_append_levels_parity(fsq, levels, n, C, G):
     g = synth.rng(102, n + levels, C + G)
