@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-recon", action="store_true",
                     help="skip the key-reconstruction comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-launch-floor", action="store_true",
+                    help="skip timing the step's launch chain of trivial kernels")
     ap.add_argument("--no-layer-batched", action="store_true",
                     help="skip the layer-batched measurement (all layers' attention in one call)")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
@@ -316,6 +318,36 @@ def append_prefill(w, torch, calls=40, eager=False):
             "traffic": traffic_from_append_profile(w),
             "timing": (f"{calls} eager calls" if eager else f"{calls} calls in one HIP graph")
                       + f" over {reps} replicas of x, events around them"}
+
+
+def launch_floor(w, torch, kernels_per_layer=3, steps=30):
+    """Time a step's launch chain alone: layers x kernels_per_layer dependent
+    trivial kernels (fill_ of a 512 KB buffer, 256 CTAs each) replayed from one
+    HIP graph, the step's own launch pattern with no work behind it."""
+    bufs = [torch.empty(256 * 512, dtype=torch.float32, device="cuda") for _ in range(kernels_per_layer)]
+    def chain():
+        for l in range(w.layers):
+            for i, b in enumerate(bufs):
+                b.fill_(float(l * kernels_per_layer + i))
+    chain()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    n = w.layers * kernels_per_layer
+    return {"what": f"{w.layers} layers x {kernels_per_layer} dependent trivial kernels (256 CTAs each) "
+                    "in one HIP graph: the step's launch chain without its work",
+            "kernels_per_step": n, "ms_per_step": ms, "us_per_kernel": ms * 1e3 / n}
 
 
 def copy_probe(torch, mib):
@@ -889,6 +921,7 @@ def main():
             r = recon_comparison(w2, torch, fsq_ms[name], rope=True)
             if r is not None:
                 recon[name + "_rope"] = r
+    floor = None if args.no_launch_floor else launch_floor(w, torch)
     batched = {}
     if not args.no_layer_batched:
         for name in [n for n in [args.workload] + [s for s in args.also.split(",") if s] if n in COMPARED]:
@@ -942,6 +975,7 @@ def main():
         "sdpa_comparison": sdpa,
         "recon_comparison": recon,
         "layer_batched": batched,
+        "launch_floor": floor,
     }
     print(json.dumps(line))
 
