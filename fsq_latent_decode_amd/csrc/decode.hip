@@ -241,7 +241,6 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
     // rows past n_q up to the 32-head padding are zero: the CTAs of kv head 0
     // clear this column block of them, one 16-byte store per thread (at most
     // 31 rows x 8 chunks; the block's columns are a contiguous 128-byte run)
-#ifndef FSQ_ABSORB_SERIAL_PAD
     if (g == 0) {
         const int npad = nqp - n_q, pr = tid >> 3, pc = cblk * kAbsorbCols + 8 * (tid & 7);
         if (pr < npad && pc < GP) {
@@ -250,15 +249,6 @@ __device__ __attribute__((always_inline)) inline void absorb_rows(int g, int cbl
             if (qlo) *reinterpret_cast<u32x4 *>(qt + qlo + o) = u32x4{};
         }
     }
-#else
-    if (g == 0 && dg == 0)
-        for (int c = 0; c < VW; ++c)
-            if (k0 + c < GP)
-                for (int h = n_q; h < nqp; ++h) {
-                    qt[((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
-                    if (qlo) qt[qlo + ((size_t)b * nqp + h) * GP + k0 + c] = (_Float16)0.0f;
-                }
-#endif
     float w[RR][VW];
 #pragma unroll
     for (int i = 0; i < RR; ++i) {
