@@ -255,6 +255,9 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     (2, 32, 8, 128, 64, 65600, [65600, 40001]),
     (1, 32, 8, 128, 84, 131072, [130999]),
     (3, 16, 8, 128, 90, 50000, [50000, 9, 33333]),
+    # one query head per kv head: four sequences share an absorption CTA (the
+    # last group partial), 24 padded query rows each
+    (5, 8, 8, 64, 64, 300, [300, 1, 0, 77, 256]),
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -670,6 +673,8 @@ def check_step(got_codes, got_out, x, E, q, packed, W, lens, n_kv, G):
     (5, 4096, 32, 8, 128, 256, 400, [400, 17, 1, 0, 250]),          # 8 per CTA
     (9, 64, 8, 2, 64, 96, 100, [100, 5, 0, 1, 64, 33, 99, 100, 2]),  # two CTAs of 8 tokens per byte
     (2, 64, 8, 1, 64, 30, 50, [60, 50]),                            # length > cap: no append, clamped
+    (6, 256, 16, 8, 128, 64, 200, [200, 3, 0, 150, 1, 77]),         # 2 sequences per absorption CTA
+    (5, 128, 4, 4, 64, 32, 90, [90, 1, 50, 0, 2]),                  # 4 per absorption CTA, last group of 1
 ])
 def test_decode_step_parity(fsq, B, C, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 11 + cap + B, B, n_q, n_kv, d_h, G, cap, lens)
