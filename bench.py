@@ -310,14 +310,58 @@ def append_prefill(w, torch, calls=40, eager=False):
     flops = 2.0 * n * w.G * w.C
     ach = nbytes / (us * 1e-6) / 1e9
     codes0 = codes[0].cpu().numpy()
+    floor = append_load_floor(w, torch, xs, Ed, calls)
     return codes0, {"workload": w.name, "tokens": n, "C": w.C, "G": w.G, "us_per_call": us,
             "tokens_per_s": n / (us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "bytes_per_call": nbytes,
                          "mfma_frac": flops / (us * 1e-6) / (MFMA_FP16_PEAK_TFLOPS * 1e12)},
             "traffic": traffic_from_append_profile(w),
+            "load_floor": floor,
             "timing": (f"{calls} eager calls" if eager else f"{calls} calls in one HIP graph")
                       + f" over {reps} replicas of x, events around them"}
+
+
+def append_load_floor(w, torch, xs, Ed, calls):
+    """The prefill append's memory side alone: a load-only kernel (the probe
+    library built beside libfsq.so) that issues the append kernel's per-CU reads
+    of x and of E, timed like the append (HIP graph of `calls` launches over the
+    replicas of x): x and E together, x alone, E alone."""
+    import ctypes
+    path = os.path.join(ROOT, "fsq_latent_decode_amd", "lib", "libfsq_probe.so")
+    if not os.path.exists(path):
+        return {"skipped": "libfsq_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.fsq_probe_append_loads.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fsq_probe_append_loads.restype = ctypes.c_int
+    n = xs[0].shape[0]
+    out = torch.empty((n // 32) * 512, dtype=torch.int32, device="cuda")
+    res = {"what": "load-only kernel with the append's per-CU reads (32 tokens per CTA: the CTA's x rows "
+                   "and all GP rows of E, 512-byte row segments, rotated batch order, 16 loads in flight "
+                   "per wave)"}
+    for mode, key in ((0, "x_and_E_us"), (1, "x_only_us"), (2, "E_only_us")):
+        def launch(i):
+            rc = lib.fsq_probe_append_loads(mode, xs[i % len(xs)].data_ptr(), Ed.data_ptr(), n, w.C, w.G,
+                                            out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"fsq_probe_append_loads returned {rc}")
+        for i in range(len(xs)):
+            launch(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                launch(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        res[key] = t0.elapsed_time(t1) * 1e3 / calls
+    return res
 
 
 def launch_floor(w, torch, kernels_per_layer=3, steps=30):
