@@ -208,6 +208,47 @@ def test_append_prefill_chunk_g84(fsq):
     print(f"g84 prefill chunk: {flips} of {x.shape[0] * w.G} codes at fp32 ties (largest tie distance {dist:.2e})")
 
 
+@pytest.mark.parametrize("G,levels", [(256, 16), (168, 4)])
+def test_append_prefill_chunk_wide(fsq, G, levels):
+    """An 8192 x 4096 prefill chunk at the widths whose append takes 128-wide
+    k-batches and sums the waves in passes of 128 codes: G = 256 (4 bits, the
+    32x operating point) and G = 168 at 2 bits (the G=84 byte budget)."""
+    g = synth.rng(104, G, levels)
+    x = synth.normal_bf16(g, (8192, 4096))
+    E = synth.normal_bf16(g, (G, 4096), 1.0 / 64.0)
+    got = run_append(fsq, x, E, levels=levels)
+    flips, dist = check_codes(got, x, E, G, levels)
+    print(f"G={G} L={levels} prefill chunk: {flips} of {x.shape[0] * G} codes at fp32 ties "
+          f"(largest tie distance {dist:.2e})")
+
+
+@pytest.mark.parametrize("G", [84, 256])
+def test_append_position_in_call(fsq, G):
+    """A token's codes do not depend on where it sits in the call beyond the tie
+    rule: the CTA of 32 tokens that holds it starts its k-batches at its own
+    index mod C / KPB, so the same rows appended after 32 and after 40 other
+    rows go through other CTAs, other batch orders and other tile rows. Both
+    calls are checked against the oracle, and against each other, where a code
+    may differ only if one of them is a flip."""
+    g = synth.rng(105, G, 0)
+    n, C = 300, 2048
+    x = synth.normal_bf16(g, (n + 40, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    a = run_append(fsq, x[40:], E)                       # rows 0.. of the call
+    b = run_append(fsq, x[8:], E)[32:]                   # the same rows after 32 others
+    c = run_append(fsq, x, E)[40:]                       # ... and after 40 others
+    for got in (a, b, c):
+        check_codes(got, x[40:], E, G)
+    P = a.shape[1]
+    da = orc.unpack_codes(a, G, 4).astype(int)
+    for other in (b, c):
+        do = orc.unpack_codes(other, G, 4).astype(int)
+        assert np.all(np.abs(da - do) <= 1)
+        allowed = 2 * max(1, int(FLIP_RATE * da.size))   # each side's tie flips against the oracle
+        assert np.count_nonzero(da != do) <= allowed, "positions in the call changed codes beyond the tie flips"
+    assert a.shape == (n, P)
+
+
 # ------------------------------------------------------------------ decode
 def run_decode(fsq, q_bits, packed, W_bits, lens, n_kv, workspace=None):
     q = dev_bf16(q_bits)
