@@ -80,7 +80,10 @@ const char *fsq_status_string(int status);
  * Arithmetic: bf16 products accumulated in fp32 (MFMA for n_tokens >= 32,
  * vector FMA below), bound and round in fp32. Compared with an exact fp64
  * evaluation a code can differ by +-1 only where u~ lies within fp32 rounding
- * of a half-integer.
+ * of a half-integer. The fp32 summation order depends on the token's place in
+ * the call (which 32-token block holds it), so such a code can also differ
+ * between calls that place the same token differently; repeating a call gives
+ * the same bits.
  * Errors: FSQ_ERR_NULL (x, E or codes NULL with n_tokens > 0),
  *         FSQ_ERR_SHAPE (n_tokens < 0, C < 1, G < 1), FSQ_ERR_UNSUPPORTED
  *         (C % 8 != 0, G > FSQ_MAX_G, x or E not 16-byte aligned), FSQ_ERR_HIP.
