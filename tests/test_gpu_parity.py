@@ -235,6 +235,7 @@ def test_append_position_in_call(fsq, G):
     x = synth.normal_bf16(g, (n + 40, C))
     E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
     a = run_append(fsq, x[40:], E)                       # rows 0.. of the call
+    assert np.array_equal(a, run_append(fsq, x[40:], E)), "a repeated append call changed bits"
     b = run_append(fsq, x[8:], E)[32:]                   # the same rows after 32 others
     c = run_append(fsq, x, E)[40:]                       # ... and after 40 others
     for got in (a, b, c):
