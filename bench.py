@@ -45,8 +45,8 @@ CPU_BASELINE_WORKLOADS = ("qwen3_8b_g256", "qwen3_8b_g84", "qwen3_1p7b_ragged", 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_8b_g256", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--also", default="qwen3_8b_g84,qwen3_1p7b_ragged,qwen3_8b_g84_1m,qwen3_8b_g32,"
                                       "qwen3_8b_g20,qwen3_8b_l4_g168,qwen3_8b_l256_g42",
