@@ -300,6 +300,10 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     # one query head per kv head: four sequences share an absorption CTA (the
     # last group partial), 24 padded query rows each
     (5, 8, 8, 64, 64, 300, [300, 1, 0, 77, 256]),
+    # widths above 128 with 129..256 splits: the one-barrier merge with 8 splits
+    # per lane (196 splits: the last lanes' slots partly past the sequence)
+    (1, 32, 8, 128, 256, 65536, [65536]),
+    (1, 32, 8, 128, 200, 100000, [99999]),
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -464,6 +468,7 @@ def run_decode_levels(fsq, q_bits, packed, W_bits, lens, n_kv, levels):
     (1, 32, 8, 128, 32, 70000, [70000]),
     (2, 32, 8, 128, 64, 65600, [65600, 40001]),  # 8-wave split CTAs (widths 64, 96 on long work)
     (1, 32, 8, 128, 84, 131072, [130999]),
+    (1, 32, 8, 128, 168, 131072, [131072]),      # the 2-bit operating point's width: 256 splits, 8 per merge lane
 ])
 def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
     g = synth.rng(210, levels, G + cap)
