@@ -304,6 +304,10 @@ def decode_case(seed, B, n_q, n_kv, d_h, G, cap, lens):
     # per lane (196 splits: the last lanes' slots partly past the sequence)
     (1, 32, 8, 128, 256, 65536, [65536]),
     (1, 32, 8, 128, 200, 100000, [99999]),
+    # the narrowest latents: one or two codes per token, 30-31 zero-padded
+    # coordinates of the 32-wide operand
+    (2, 8, 2, 64, 1, 200, [200, 3]),
+    (1, 16, 8, 128, 2, 5000, [4999]),
 ])
 def test_decode_parity(fsq, B, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 7 + cap, B, n_q, n_kv, d_h, G, cap, lens)
@@ -469,6 +473,7 @@ def run_decode_levels(fsq, q_bits, packed, W_bits, lens, n_kv, levels):
     (2, 32, 8, 128, 64, 65600, [65600, 40001]),  # 8-wave split CTAs (widths 64, 96 on long work)
     (1, 32, 8, 128, 84, 131072, [130999]),
     (1, 32, 8, 128, 168, 131072, [131072]),      # the 2-bit operating point's width: 256 splits, 8 per merge lane
+    (2, 8, 2, 64, 1, 300, [300, 2]),               # one code per token
 ])
 def test_decode_levels_parity(fsq, levels, B, n_q, n_kv, d_h, G, cap, lens):
     g = synth.rng(210, levels, G + cap)
@@ -722,6 +727,7 @@ def check_step(got_codes, got_out, x, E, q, packed, W, lens, n_kv, G):
     (2, 64, 8, 1, 64, 30, 50, [60, 50]),                            # length > cap: no append, clamped
     (6, 256, 16, 8, 128, 64, 200, [200, 3, 0, 150, 1, 77]),         # 2 sequences per absorption CTA
     (5, 128, 4, 4, 64, 32, 90, [90, 1, 50, 0, 2]),                  # 4 per absorption CTA, last group of 1
+    (3, 256, 8, 2, 64, 1, 120, [120, 1, 60]),                       # one code per token (half a byte)
 ])
 def test_decode_step_parity(fsq, B, C, n_q, n_kv, d_h, G, cap, lens):
     q, packed, W, lens = decode_case(G * 11 + cap + B, B, n_q, n_kv, d_h, G, cap, lens)
