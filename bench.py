@@ -171,22 +171,23 @@ class Model:
 
     def step(self, r, ev=None, two_call=False):
         """One decode step over replica r: per layer, one fsq_decode_step call
-        (append of the new token at row T - 1 + attention). With ev (eager only),
+        (append of the new token at row T - 1 + attention; levels as the
+        workload's codes). With ev (eager only),
         ev[l] = (start, stop) events bracket layer l's split-K kernel; that form
         issues the same work as fsq_append + fsq_decode_attn_timed (the split-K
         kernel and its inputs are the same)."""
         fsq, w = self.fsq, self.w
         for l, d in enumerate(self.reps[r]):
-            if w.levels != 16:   # 2- / 8-bit codes: append + attention calls
+            if ev is None and not two_call:
+                fsq.fsq_decode_step(d["x"], d["E"], d["q"], d["codes"], d["W"], self.lens, d["out"],
+                                    w.n_kv, workspace=self.ws, levels=w.levels)
+                continue
+            if w.levels != 16:   # 2- / 8-bit codes, timed or two-call form: append + attention calls
                 for b in range(w.batch):
                     T = int(self.lens_np[b])
                     fsq.fsq_append(d["x"][b:b + 1], d["E"], d["codes"][b, T - 1:T], levels=w.levels)
                 fsq.fsq_decode_attn_levels(d["q"], d["codes"], d["W"], self.lens, d["out"], w.n_kv, w.levels,
                                            workspace=self.ws, split_events=None if ev is None else ev[l])
-                continue
-            if ev is None and not two_call:
-                fsq.fsq_decode_step(d["x"], d["E"], d["q"], d["codes"], d["W"], self.lens, d["out"],
-                                    w.n_kv, workspace=self.ws)
                 continue
             for b in range(w.batch):
                 T = int(self.lens_np[b])

@@ -20,7 +20,8 @@ _LIB_PATH = os.environ.get("FSQ_LIBRARY_PATH") or os.path.join(
 EXPORTS = ("fsq_status_string", "fsq_append", "fsq_decode_workspace_bytes", "fsq_decode_attn",
            "fsq_decode_attn_timed", "fsq_decode_step", "fsq_decode_attn_recon",
            "fsq_decode_attn_rope", "fsq_append_levels", "fsq_decode_attn_levels",
-           "fsq_decode_attn_levels_timed", "fsq_decode_plan_info", "fsq_decode_attn_noalloc")
+           "fsq_decode_attn_levels_timed", "fsq_decode_plan_info", "fsq_decode_attn_noalloc",
+           "fsq_decode_step_levels")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # FSQ_NOALLOC_SCRATCH_BYTES in include/fsq.h
 
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.fsq_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                       vp, sz, vp]
         L.fsq_decode_step.restype = ctypes.c_int
+        L.fsq_decode_step_levels.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             i64, vp, sz, vp]
+        L.fsq_decode_step_levels.restype = ctypes.c_int
         L.fsq_decode_attn_recon.argtypes = L.fsq_decode_attn.argtypes
         L.fsq_decode_attn_recon.restype = ctypes.c_int
         L.fsq_decode_plan_info.argtypes = [i32, i32, i32, i64, vp, vp, vp]
@@ -209,13 +213,16 @@ def _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels=16):
 
 def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes: torch.Tensor,
                     W_kv: torch.Tensor, seq_lens: torch.Tensor, out: torch.Tensor, n_kv: int,
-                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                    workspace: torch.Tensor | None = None, stream=None, levels: int = 16) -> torch.Tensor:
     """One decode step of one layer: codes[b, seq_lens[b] - 1] = pack(FSQ(E x_new[b]))
     for every sequence with 1 <= seq_lens[b] <= cap, then out = attention over the
     cache as in fsq_decode_attn. seq_lens already counts the new token.
 
-    x_new [B, C] bf16, E [G, C] bf16; the other arguments as fsq_decode_attn."""
-    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv)
+    x_new [B, C] bf16, E [G, C] bf16; the other arguments as fsq_decode_attn
+    (levels = 4 / 256: 2- / 8-bit codes, as fsq_decode_attn_levels)."""
+    if levels not in LEVEL_BITS:
+        raise ValueError(f"levels must be one of {sorted(LEVEL_BITS)}")
+    B, n_q, d_h, G, cap = _check_decode_args(q, codes, W_kv, seq_lens, out, n_kv, levels)
     _dev(x_new, "x_new", torch.bfloat16, 2)
     _dev(E, "E", torch.bfloat16, 2)
     C = x_new.shape[1]
@@ -223,10 +230,17 @@ def fsq_decode_step(x_new: torch.Tensor, E: torch.Tensor, q: torch.Tensor, codes
         raise ValueError(f"x_new must be [{B}, C] and E [{G}, C], got {tuple(x_new.shape)}, "
                          f"{tuple(E.shape)}")
     workspace = _call_workspace(workspace, B, n_q, G, cap, q.device, stream)
-    rc = lib().fsq_decode_step(x_new.data_ptr(), E.data_ptr(), q.data_ptr(), codes.data_ptr(),
-                               W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q, n_kv,
-                               d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
-    _check(rc, "fsq_decode_step")
+    if levels == 16:
+        rc = lib().fsq_decode_step(x_new.data_ptr(), E.data_ptr(), q.data_ptr(), codes.data_ptr(),
+                                   W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q, n_kv,
+                                   d_h, G, cap, workspace.data_ptr(), workspace.numel(), _stream(stream))
+        _check(rc, "fsq_decode_step")
+    else:
+        rc = lib().fsq_decode_step_levels(x_new.data_ptr(), E.data_ptr(), q.data_ptr(), codes.data_ptr(),
+                                          W_kv.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, C, n_q,
+                                          n_kv, d_h, G, levels, cap, workspace.data_ptr(), workspace.numel(),
+                                          _stream(stream))
+        _check(rc, "fsq_decode_step_levels")
     return out
 
 

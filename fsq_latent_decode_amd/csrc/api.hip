@@ -177,6 +177,16 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
                          workspace_bytes, stream, nullptr, nullptr, x_new, E, C);
 }
 
+int fsq_decode_step_levels(const uint16_t *x_new, const uint16_t *E, const uint16_t *q, uint8_t *codes,
+                           const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int32_t batch,
+                           int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G, int32_t levels,
+                           int64_t seq_cap, void *workspace, size_t workspace_bytes, void *stream) {
+    const int v = fsq::validate_step_append(x_new, E, batch, C, n_q, n_kv, d_h, G, seq_cap);
+    if (v != FSQ_OK) return v;
+    return decode_common(q, codes, W_kv, seq_lens, out, batch, n_q, n_kv, d_h, G, seq_cap, workspace,
+                         workspace_bytes, stream, nullptr, nullptr, x_new, E, C, levels);
+}
+
 static int recon_common(const uint16_t *q, const uint8_t *codes, const uint16_t *W_kv,
                         const int32_t *seq_lens, uint16_t *out, int32_t batch, int32_t n_q,
                         int32_t n_kv, int32_t d_h, int32_t G, int64_t seq_cap, void *workspace,

@@ -339,47 +339,51 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t *__restrict_
 // [0, n_app) append the new token of each sequence (output byte j = bx % P of
 // tokens (bx / P) NT ..) at row seq_lens[b] - 1 of its cache, the rest absorb
 // the queries (kv head, 64-column block, sequence). The split kernel that
-// follows sees the appended rows.
+// follows sees the appended rows. CPB codes per byte: 2 (4-bit codes), 4
+// (2-bit) or 1 (8-bit, whose absorption also writes the second term of q~ at
+// qt + qlo).
 struct StepAppend {
     const uint16_t *x_new, *E;
     uint8_t *codes;
     int C;
-    FsqQuant fq;   // L = 16
+    FsqQuant fq;   // the code width's L
 };
 
-template <int NT, int VW>
+template <int NT, int VW, int CPB>
 __global__ __launch_bounds__(256) void step_prep_kernel(StepAppend ap, const int32_t *__restrict__ seq_lens,
                                                         int64_t seq_cap, int batch, int n_app,
                                                         const uint16_t *__restrict__ q,
                                                         const uint16_t *__restrict__ W_kv,
                                                         _Float16 *__restrict__ qt, int G, int GP,
                                                         int n_q, int nqp, int n_kv, int d_h, float scale,
-                                                        float odd_scale) {
+                                                        float odd_scale, size_t qlo) {
     const int bx = blockIdx.x;
-    const int P = bytes_per_token(G);
+    const int P = bytes_per_token_b(G, 8 / CPB);
     if (bx < n_app) {
-        append_gemv_body<NT, 2>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.fq,
-                             seq_lens, seq_cap);
+        append_gemv_body<NT, CPB>(bx % P, (bx / P) * NT, ap.x_new, ap.E, ap.codes, batch, ap.C, G, ap.fq,
+                                  seq_lens, seq_cap);
     } else {
         const int ncb = (GP + kAbsorbCols - 1) / kAbsorbCols;
         int r = bx - n_app;
         const int g = r % n_kv;
         r /= n_kv;
-        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, 4, 0);
+        absorb_body<VW>(g, r % ncb, r / ncb, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, 8 / CPB,
+                        qlo);
     }
 }
 
-template <int NT>
+template <int NT, int CPB>
 static void launch_step_prep_nt(int vw, dim3 grid, hipStream_t st, const StepAppend &ap,
                                 const int32_t *seq_lens, int64_t seq_cap, int batch, int n_app,
                                 const uint16_t *q, const uint16_t *W_kv, _Float16 *qt, int G, int GP,
-                                int n_q, int nqp, int n_kv, int d_h, float scale, float odd_scale) {
-#define FSQ_PREP_ARGS ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale
+                                int n_q, int nqp, int n_kv, int d_h, float scale, float odd_scale,
+                                size_t qlo) {
+#define FSQ_PREP_ARGS ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, GP, n_q, nqp, n_kv, d_h, scale, odd_scale, qlo
     switch (vw) {
-        case 8: step_prep_kernel<NT, 8><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
-        case 4: step_prep_kernel<NT, 4><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
-        case 2: step_prep_kernel<NT, 2><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
-        default: step_prep_kernel<NT, 1><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS);
+        case 8: step_prep_kernel<NT, 8, CPB><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        case 4: step_prep_kernel<NT, 4, CPB><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        case 2: step_prep_kernel<NT, 2, CPB><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS); break;
+        default: step_prep_kernel<NT, 1, CPB><<<grid, 256, 0, st>>>(FSQ_PREP_ARGS);
     }
 #undef FSQ_PREP_ARGS
 }
@@ -2361,19 +2365,28 @@ hipError_t launch_decode(const DecodePlan &pl, const uint16_t *q, const uint8_t 
                                                                    : 1;
     if (pl.S > 0 && x_new) {
         // decode step: append + absorb in one launch
-        const StepAppend ap{x_new, E, const_cast<uint8_t *>(codes), C, host_fsq_quant(16)};
+        const StepAppend ap{x_new, E, const_cast<uint8_t *>(codes), C, host_fsq_quant(levels)};
         const int nt = gemv_tokens_per_cta(batch);
-        const int n_app = bytes_per_token(G) * ((batch + nt - 1) / nt);
+        const int n_app = bytes_per_token_b(G, bits) * ((batch + nt - 1) / nt);
         const int n_abs = n_kv * ((pl.GP + kAbsorbCols - 1) / kAbsorbCols) * batch;
         const dim3 grid((unsigned)(n_app + n_abs));
-#define FSQ_PREP_CALL(NT) \
-    launch_step_prep_nt<NT>(vw, grid, st, ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd)
-        switch (nt) {
-            case 1: FSQ_PREP_CALL(1); break;
-            case 2: FSQ_PREP_CALL(2); break;
-            case 4: FSQ_PREP_CALL(4); break;
-            default: FSQ_PREP_CALL(kGemvTokens);
+#define FSQ_PREP_CALL(NT, CPB) \
+    launch_step_prep_nt<NT, CPB>(vw, grid, st, ap, seq_lens, seq_cap, batch, n_app, q, W_kv, qt, G, pl.GP, n_q, pl.nqp, n_kv, d_h, scale, odd, qlo)
+#define FSQ_PREP_NT(CPB)                                  \
+        switch (nt) {                                     \
+            case 1: FSQ_PREP_CALL(1, CPB); break;         \
+            case 2: FSQ_PREP_CALL(2, CPB); break;         \
+            case 4: FSQ_PREP_CALL(4, CPB); break;         \
+            default: FSQ_PREP_CALL(kGemvTokens, CPB);     \
         }
+        if (bits == 2) {
+            FSQ_PREP_NT(4)
+        } else if (bits == 8) {
+            FSQ_PREP_NT(1)
+        } else {
+            FSQ_PREP_NT(2)
+        }
+#undef FSQ_PREP_NT
 #undef FSQ_PREP_CALL
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (pl.S > 0) {

@@ -266,6 +266,20 @@ int fsq_decode_step(const uint16_t *x_new, const uint16_t *E, const uint16_t *q,
                     int64_t seq_cap, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fsq_decode_step_levels - fsq_decode_step for L = levels per coordinate (4,
+ * 16 or 256: 2-, 4- or 8-bit codes, rows of ceil(G b / 8) bytes; the slides'
+ * backup frame "the grid size is an allocation choice"). The append of each
+ * new token is fsq_append_levels' and the attention fsq_decode_attn_levels';
+ * the results are bit-identical to those two calls. fsq_decode_step is
+ * fsq_decode_step_levels with levels = 16.
+ * Errors: as fsq_decode_step; FSQ_ERR_UNSUPPORTED for another number of levels.
+ */
+int fsq_decode_step_levels(const uint16_t *x_new, const uint16_t *E, const uint16_t *q, uint8_t *codes,
+                           const uint16_t *W_kv, const int32_t *seq_lens, uint16_t *out, int32_t batch,
+                           int32_t C, int32_t n_q, int32_t n_kv, int32_t d_h, int32_t G, int32_t levels,
+                           int64_t seq_cap, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * fsq_decode_attn_recon - the same attention as fsq_decode_attn, computed the
  * way the pages' kernel does: keys are rebuilt per 32-token tile on chip,
  * K_tile = Z_tile W_k,g^T (Eq. 5 without key norm and RoPE), and scored against

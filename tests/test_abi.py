@@ -133,6 +133,20 @@ def test_decode_step_validation_before_any_hip_call(args, status):
 
 
 @needs_lib
+@pytest.mark.parametrize("levels,C,G,status", [
+    (8, 64, 256, "FSQ_ERR_UNSUPPORTED"),    # not 4, 16 or 256 levels
+    (3, 64, 84, "FSQ_ERR_UNSUPPORTED"),
+    (4, 60, 84, "FSQ_ERR_UNSUPPORTED"),     # C % 8 != 0, as for the 4-bit step
+    (256, 0, 42, "FSQ_ERR_SHAPE"),
+    (4, 64, 300, "FSQ_ERR_UNSUPPORTED"),    # G > FSQ_MAX_G
+])
+def test_decode_step_levels_validation_before_any_hip_call(levels, C, G, status):
+    rc = fsq.lib().fsq_decode_step_levels(256, 256, 256, 256, 256, 256, 256, 1, C, 32, 8, 128, G, levels,
+                                          16, 256, 1 << 20, None)
+    assert rc == getattr(fsq, status)
+
+
+@needs_lib
 @pytest.mark.parametrize("args,status", [
     # (q, codes, W, lens, out, batch, n_q, n_kv, d_h, G, cap, ws, ws_bytes)
     ((256, 256, 256, 256, 256, 0, 32, 8, 128, 256, 16, 256, 1 << 20), fsq.FSQ_ERR_SHAPE),

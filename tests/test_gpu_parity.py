@@ -741,6 +741,63 @@ def test_decode_step_parity(fsq, B, C, n_q, n_kv, d_h, G, cap, lens):
     assert np.array_equal(got_out, two_out)
 
 
+@pytest.mark.parametrize("levels", [4, 256])
+@pytest.mark.parametrize("B,C,n_q,n_kv,d_h,G,cap,lens", [
+    (1, 1024, 16, 8, 128, 64, 1024, [1024]),
+    (3, 256, 12, 4, 96, 37, 300, [0, 300, 299]),                    # odd G, an empty sequence
+    (5, 4096, 32, 8, 128, 168, 400, [400, 17, 1, 0, 250]),          # the 2-bit operating point's width
+    (9, 64, 8, 2, 64, 42, 100, [100, 5, 0, 1, 64, 33, 99, 100, 2]),  # the 8-bit operating point's width
+    (2, 64, 8, 1, 64, 30, 50, [60, 50]),                            # length > cap: no append
+    (3, 256, 8, 2, 64, 1, 120, [120, 1, 60]),                       # one code per token
+])
+def test_decode_step_levels_parity(fsq, levels, B, C, n_q, n_kv, d_h, G, cap, lens):
+    """fsq_decode_step with 2- and 8-bit codes: the appended rows against the
+    oracle (tie rule), every other row untouched, the output against the
+    oracle's decode of the oracle-appended cache, and bit-identical results to
+    fsq_append (one token per call) followed by fsq_decode_attn_levels."""
+    bits = orc.bits_of_levels(levels)
+    g = synth.rng(212, levels * 7 + B, G + cap)
+    q = synth.normal_bf16(g, (B, n_q, d_h))
+    W = synth.normal_bf16(g, (2 * n_kv * d_h, G), 1.0 / math.sqrt(G))
+    packed = synth.uniform_code_bytes(g, (B, cap), G, bits)
+    x = synth.normal_bf16(g, (B, C))
+    E = synth.normal_bf16(g, (G, C), 1.0 / math.sqrt(C))
+    lens = np.asarray(lens, np.int32)
+    lens_d = torch.from_numpy(lens).cuda()
+    codes = dev_u8(packed)
+    out = torch.empty((B, n_q, d_h), dtype=torch.bfloat16, device="cuda")
+    fsq.fsq_decode_step(dev_bf16(x), dev_bf16(E), dev_bf16(q), codes, dev_bf16(W), lens_d, out, n_kv,
+                        levels=levels)
+    codes2 = dev_u8(packed)
+    for b, T in enumerate(lens):
+        if 1 <= T <= cap:
+            fsq.fsq_append(dev_bf16(x[b:b + 1]), dev_bf16(E), codes2[b, T - 1:T], levels=levels)
+    out2 = torch.empty_like(out)
+    fsq.fsq_decode_attn_levels(dev_bf16(q), codes2, dev_bf16(W), lens_d, out2, n_kv, levels)
+    torch.cuda.synchronize()
+    got_codes = codes.cpu().numpy()
+    assert np.array_equal(got_codes, codes2.cpu().numpy()), "step and two-call appends differ"
+    assert torch.equal(out, out2), "step and two-call outputs differ"
+    app = [b for b, T in enumerate(lens) if 1 <= T <= cap]
+    ref_cache = packed.copy()
+    if app:
+        rows = np.stack([got_codes[b, lens[b] - 1] for b in app])
+        check_codes(rows, x[app], E, G, levels)
+        new = orc.pack_codes(orc.encode(synth.bf16_bits_to_f64(x[app]), synth.bf16_bits_to_f64(E), levels),
+                             bits)
+        for i, b in enumerate(app):
+            ref_cache[b, lens[b] - 1] = new[i]
+    mask = np.ones(packed.shape[:2], bool)
+    for b in app:
+        mask[b, lens[b] - 1] = False
+    assert np.array_equal(got_codes[mask], packed[mask]), "a row other than the new token's changed"
+    eff = np.minimum(np.maximum(lens, 0), cap)
+    ref = orc.decode_attn(synth.bf16_bits_to_f64(q), ref_cache, synth.bf16_bits_to_f64(W), eff, n_kv, G,
+                          levels=levels)
+    check_decode(out.float().cpu().numpy().astype(np.float64), ref, eff,
+                 f"decode step L={levels} B={B} G={G} cap={cap}")
+
+
 @pytest.mark.parametrize("name", ["qwen3_8b_g256", "qwen3_8b_g84"])
 def test_decode_step_full_size_layer(fsq, name):
     """One decode step of layer 0 of the Qwen3-8B-shaped workloads at full context,
