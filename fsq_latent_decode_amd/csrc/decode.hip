@@ -1015,9 +1015,12 @@ __device__ inline int stream_dyn_chunk(int64_t total, int ncta, int nseq, int ch
     // By an fp64 division: total < 2^37 and n <= 2^10, so the correctly rounded
     // quotient is within 2^-15 of the exact one, whose fraction is 0 or at
     // least 2^-10: its floor is the integer quotient
+    // rounded up to whole rounds by a mask: q, a round of 32 tokens times the
+    // streaming kernel's 4 or 8 waves, is a power of two (a 64-bit division by
+    // a runtime value costs dozens of instructions in every wave)
     const int n = ncta - nseq + 1;
     int64_t c = (int64_t)floor((double)(total + n - 1) / (double)n);
-    c = (c + q - 1) / q * q;
+    c = (c + q - 1) & ~(q - 1);
     return (int)(c < chunk_min ? chunk_min : c);
 }
 // Cross-lane arithmetic without LDS (DPP and lane swaps; the compiler adds the

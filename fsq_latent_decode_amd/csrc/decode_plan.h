@@ -31,7 +31,7 @@ inline int split_waves(int GP, int64_t work) {
 // kStreamMinTiles tiles of 32 tokens. (The key-reconstruction variants use
 // 4-wave CTAs at every width: kStreamWaves.)
 constexpr int kStreamWaves = 4;
-inline int stream_waves(int GP) { return GP < 128 ? 8 : 4; }
+inline int stream_waves(int GP) { return GP < 128 ? 8 : 4; }   // 32 x this is a power of two (the device split rounds by masks)
 constexpr int kStreamMinTiles = 4;
 // Streaming calls of up to kDynMaxBatch sequences split on the device from the
 // actual lengths (one lane per sequence there); the chunk is then at least
