@@ -2127,9 +2127,19 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge1_kernel(
     for (int j = 0; j < 8; ++j) a[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < RS; ++i) {
-        const bool ok = sl + SEG * i < ns;
+        if constexpr (SEG == 32) {
+            // widths above 128: a row past the sequence's splits (weight 0) is
+            // cleared before use, once per row rather than per product, so that
+            // each term is one mixed-precision FMA of the fp16 value (measured
+            // faster there, slower with 64-lane segments)
+            const half8 vi = sl + SEG * i < ns ? v[i] : half8{};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] += ok ? c[i] * (float)v[i][j] : 0.0f;
+            for (int j = 0; j < 8; ++j) a[j] = fmaf(c[i], (float)vi[j], a[j]);
+        } else {
+            const bool ok = sl + SEG * i < ns;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] += ok ? c[i] * (float)v[i][j] : 0.0f;
+        }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) a[j] = seg_sum<SEG>(a[j]);
